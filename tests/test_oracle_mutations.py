@@ -1,0 +1,119 @@
+"""Test the tests: plant plausible mistakes in the oracle (on the CPU) and require a pin to fail.
+
+Each mutation replaces one oracle function with a subtly wrong variant for the
+duration of one test; the listed pin tests must then fail. This shows the pins
+are sensitive to the mistakes they are meant to catch, rather than merely
+passing.
+"""
+
+import numpy as np
+import pytest
+
+import tests.test_oracle_pins as pins
+from oracle import dsa_oracle as O
+
+
+def _no_relu(q, w, keys):
+    return w @ (q @ keys.T)
+
+
+def _reversed_head_weights(q, w, keys):
+    return w[::-1] @ np.maximum(q @ keys.T, 0.0)
+
+
+def _relu_after_sum(q, w, keys):
+    return np.maximum(w @ (q @ keys.T), 0.0)
+
+
+_orig_scores = O.indexer_scores
+
+
+def _causal_off_by_one(host, rows=None):
+    out = _orig_scores(host, rows)
+    return {r: s[:-1] for r, s in out.items()}
+
+
+def _reversed_ties(scores, k):
+    s = np.asarray(scores, dtype=np.float64)
+    n = min(k, s.shape[0])
+    order = np.lexsort((-np.arange(len(s)), -s))[:n]  # ties toward higher positions
+    out = np.full(k, -1, dtype=np.int32)
+    out[:n] = np.sort(order)
+    return out
+
+
+def _unscaled_mla(q, rows, scale, d_latent):
+    return _orig_mla_row(q, rows, 1.0, d_latent)
+
+
+_orig_mla_row = O.sparse_mla_row
+
+
+def _value_with_rope(q, rows, scale, d_latent):
+    o, lse = _orig_mla_row(q, rows, scale, rows.shape[1])
+    return o[:, -d_latent:], lse
+
+
+def _no_block_table(block_table, b, positions, page_size):
+    positions = np.asarray(positions, dtype=np.int64)
+    return positions // page_size, positions % page_size
+
+
+def _wrong_sequence_table(block_table, b, positions, page_size):
+    positions = np.asarray(positions, dtype=np.int64)
+    return block_table[0, positions // page_size].astype(np.int64), positions % page_size
+
+
+_orig_keys = O.indexer_keys
+
+
+def _fp8_scale_ignored(host, b, n):
+    h = dict(host)
+    if h["idx_k_dtype"] == "fp8":
+        h["k_scale"] = np.ones_like(np.asarray(h["k_scale"]))
+    return _orig_keys(h, b, n)
+
+
+def _e4m3_fnuz(codes):
+    # the other common e4m3 flavour: bias 8, 0x80 is NaN
+    tab = O.e4m3fn_table() / 2.0
+    tab[0x80] = np.nan
+    return tab[np.asarray(codes, dtype=np.uint8)]
+
+
+MUTATIONS = [
+    ("indexer_scores_row", _no_relu, ["test_indexer_one_hot_keys_read_out_query_columns",
+                                      "test_indexer_single_head_relu_of_dot"]),
+    ("indexer_scores_row", _reversed_head_weights, ["test_indexer_one_hot_keys_read_out_query_columns"]),
+    ("indexer_scores_row", _relu_after_sum, ["test_indexer_one_hot_keys_read_out_query_columns"]),
+    ("indexer_scores", _causal_off_by_one, ["test_indexer_causal_multi_query",
+                                            "test_mla_all_positions_equals_dense_causal_attention"]),
+    ("topk_row", _reversed_ties, ["test_topk_all_equal_scores_take_lowest_positions",
+                                  "test_topk_brute_force_and_invariants"]),
+    ("sparse_mla_row", _unscaled_mla, ["test_mla_all_positions_equals_dense_causal_attention",
+                                       "test_mla_absorption_identity"]),
+    ("sparse_mla_row", _value_with_rope, ["test_mla_value_excludes_rope_part",
+                                          "test_mla_all_positions_equals_dense_causal_attention"]),
+    ("physical_slots", _no_block_table, ["test_indexer_block_table_invariance"]),
+    ("physical_slots", _wrong_sequence_table, ["test_indexer_block_table_invariance"]),
+    ("indexer_keys", _fp8_scale_ignored, ["test_indexer_fp8_equals_bf16_on_representable_keys"]),
+    ("e4m3fn_to_f64", _e4m3_fnuz, ["test_indexer_fp8_equals_bf16_on_representable_keys"]),
+]
+
+
+def _call(name):
+    fn = getattr(pins, name)
+    if name == "test_topk_brute_force_and_invariants":
+        return fn(64, 16)
+    return fn()
+
+
+@pytest.mark.parametrize("target,mutant,caught_by", MUTATIONS,
+                         ids=[f"{t}:{m.__name__}" for t, m, _ in MUTATIONS])
+def test_mutation_is_caught(monkeypatch, target, mutant, caught_by):
+    for name in caught_by:
+        _call(name)  # passes on the real oracle
+    monkeypatch.setattr(O, target, mutant)
+    for name in caught_by:
+        with pytest.raises((AssertionError, ValueError, IndexError)):
+            _call(name)
