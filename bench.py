@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse-attention decode pass on one MI355X.
+
+One step = one pass of the whole hot path over one batch: indexer scores ->
+top-k -> one sparse-MLA call per layer (the layers share the top-k, as in
+IndexShare). Inputs are seeded synthetic data already resident in HBM.
+
+Timing: W untimed warm-up steps, then K timed steps. Before every timed step a
+1 GiB buffer is overwritten (outside the timed interval) so the 256 MB
+Infinity Cache and the L2s hold none of the step's inputs; each step is timed
+with HIP events on the stream the kernels run on, with one extra event between
+consecutive library calls to time each kernel. The whole timed loop is
+bracketed by device synchronizations.
+
+Prints one JSON line: throughput in query tokens/s, the dominant kernel's
+achieved algorithmic bandwidth against the HBM peak, and the CPU oracle's
+rate on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+WORKLOAD_DEFAULT = "decode_b32_l8k"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=WORKLOAD_DEFAULT)
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU time budget of the oracle baseline sample (0 = skip)")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------
+# algorithmic bytes (compulsory traffic through the three calls)
+# --------------------------------------------------------------------------
+
+
+def algorithmic_bytes(inp) -> dict:
+    wl = inp.wl
+    lens, qls = inp.seq_lens_host, inp.q_lens_host
+    T = inp.total_q
+    key_b = {"bf16": 2 * wl.idx_dim, "f32": 4 * wl.idx_dim, "fp8": wl.idx_dim + 4}[wl.idx_k_dtype]
+    q_b = {"bf16": 2, "f32": 4}[wl.idx_q_dtype]
+    valid = sum(sum(L - q + i + 1 for i in range(q)) for L, q in zip(lens, qls))  # (row, s) pairs
+    sel = sum(sum(min(wl.topk, L - q + i + 1) for i in range(q)) for L, q in zip(lens, qls))
+    pages = sum((L + wl.page_size - 1) // wl.page_size for L in lens)
+    e = {"bf16": 2, "f32": 4}[wl.mla_dtype]
+    row_b = (wl.d_latent + wl.d_rope) * e
+    indexer = (sum(lens) * key_b + T * wl.idx_heads * (wl.idx_dim * q_b + 4) + 4 * valid
+               + 4 * pages)
+    topk = 4 * valid + 4 * T * wl.topk
+    mla_one = (sel * row_b + T * wl.mla_heads * (wl.d_latent + wl.d_rope) * e
+               + T * wl.topk * 4 + T * wl.mla_heads * (wl.d_latent + 1) * 4)
+    flops_idx = 2 * wl.idx_heads * wl.idx_dim * valid
+    flops_mla = 2 * wl.mla_heads * (2 * wl.d_latent + wl.d_rope) * sel
+    return {"indexer": indexer, "topk": topk, "mla_per_layer": mla_one,
+            "total": indexer + topk + wl.n_layers * mla_one,
+            "flops_indexer": flops_idx, "flops_mla_per_layer": flops_mla,
+            "valid_pairs": valid, "selected_rows": sel}
+
+
+# --------------------------------------------------------------------------
+# CPU oracle baseline on a bounded sample
+# --------------------------------------------------------------------------
+
+
+def cpu_baseline(inp, budget_s: float):
+    from oracle import dsa_oracle as O
+    from workloads import host_view
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    host = host_view(inp, lazy=True)
+    rng = np.random.default_rng(0)
+    order = rng.permutation(inp.total_q)
+    done, t0 = 0, time.perf_counter()
+    for r in order:
+        s = O.indexer_scores(host, [int(r)])
+        idx = O.topk(s, inp.wl.topk)
+        for l in range(inp.wl.n_layers):
+            O.sparse_mla(host, l, idx)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "query tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {inp.total_q} query rows (random, seed 0), full pass per row "
+                      f"(indexer over all causal keys, top-{inp.wl.topk}, {inp.wl.n_layers} MLA "
+                      f"layer(s)), numpy float64, {dt:.1f} s"}
+
+
+# --------------------------------------------------------------------------
+# traffic from committed rocprofv3 counter summaries
+# --------------------------------------------------------------------------
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_attention_decode_lightning_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str, kernel: str):
+    """Per-launch HBM bytes measured with rocprofv3 counters, if taken on the current sources."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------------------
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path "
+              "shards by sequence with no exchange, see the design notes", file=sys.stderr)
+        sys.exit(2)
+    import sparse_attention_decode_lightning_amd as dsa
+    from workloads import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda:0")
+    wl = WORKLOADS[args.workload]
+    inp = make_inputs(wl, device="cuda")
+    T = inp.total_q
+    batch = dsa.Batch(inp.block_table, inp.seq_lens, inp.cu_q, T, inp.max_seq_len, inp.max_q)
+    keys = dsa.PagedCache(inp.k_cache, inp.k_scale)
+    kvs = [dsa.PagedCache(c) for c in inp.kv_cache]
+    scores = torch.empty((T, inp.max_seq_len), dtype=torch.float32, device=dev)
+    indices = torch.empty((T, wl.topk), dtype=torch.int32, device=dev)
+    outs = [torch.empty((T, wl.mla_heads, wl.d_latent), dtype=torch.float32, device=dev)
+            for _ in range(wl.n_layers)]
+    lses = [torch.empty((T, wl.mla_heads), dtype=torch.float32, device=dev)
+            for _ in range(wl.n_layers)]
+    ws_bytes = dsa.sparse_mla_workspace_size(T, wl.mla_heads, wl.d_latent, wl.topk)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    tk_bytes = dsa.topk_workspace_size(T, inp.max_seq_len, wl.topk)
+    tk_ws = torch.empty(max(tk_bytes, 16), dtype=torch.uint8, device=dev) if tk_bytes else None
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    n_ev = 3 + wl.n_layers
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        dsa.indexer_scores(batch, inp.q_idx, inp.w, keys, scores=scores)
+        if evs is not None:
+            evs[1].record(stream)
+        dsa.topk(batch, scores, wl.topk, indices=indices, workspace=tk_ws)
+        if evs is not None:
+            evs[2].record(stream)
+        for l in range(wl.n_layers):
+            dsa.sparse_mla_fwd(batch, inp.q_mla[l], kvs[l], indices, wl.d_latent, wl.scale,
+                               out=outs[l], lse=lses[l], workspace=ws)
+            if evs is not None:
+                evs[3 + l].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evsets = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.fill_(i & 0xFF)
+        step(evsets[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = np.array([[evs[j].elapsed_time(evs[j + 1]) for j in range(n_ev - 1)]
+                    for evs in evsets])  # ms, [steps, stages]
+    step_ms = per.sum(axis=1)
+    ms = float(np.mean(step_ms))
+    stage_ms = per.mean(axis=0)
+
+    # warm back-to-back figure (no flush), for context
+    torch.cuda.synchronize()
+    w0 = torch.cuda.Event(enable_timing=True)
+    w1 = torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for _ in range(args.steps):
+        step()
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / args.steps
+
+    ab = algorithmic_bytes(inp)
+    names = ["indexer", "topk"] + [f"mla_l{l}" for l in range(wl.n_layers)]
+    stage_bytes = [ab["indexer"], ab["topk"]] + [ab["mla_per_layer"]] * wl.n_layers
+    mla_ms = float(np.sum(stage_ms[2:]))
+    kern = {"indexer": (float(stage_ms[0]), ab["indexer"], "indexer_mfma_kernel"),
+            "topk": (float(stage_ms[1]), ab["topk"], "topk_kernel"),
+            "sparse_mla": (mla_ms / wl.n_layers, ab["mla_per_layer"], "sparse_mla_bf16_kernel")}
+    dom = max(kern, key=lambda k: kern[k][0] * (wl.n_layers if k == "sparse_mla" else 1))
+    d_ms, d_bytes, d_sym = kern[dom]
+    achieved = d_bytes / (d_ms * 1e-3) / 1e9
+    line = {
+        "metric": "sparse-decode query tokens/s at B=32,L=8K,topk=2048; achieved HBM GB/s",
+        "value": T / (ms * 1e-3),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.mla_dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) caches and queries, random paged block table)",
+        "config": {"workload": wl.name, "description": wl.description, "batch": wl.batch,
+                   "total_q": T, "max_seq_len": inp.max_seq_len, "topk": wl.topk,
+                   "page_size": wl.page_size, "mla_layers": wl.n_layers,
+                   "parallelism": "single GPU"},
+        "achieved_hbm_gbs": ab["total"] / (ms * 1e-3) / 1e9,
+        "algorithmic_bytes_per_step": ab["total"],
+        "stage_ms": {n: float(v) for n, v in zip(names, stage_ms)},
+        "ms_per_step_p10_p90": [float(np.percentile(step_ms, 10)),
+                                float(np.percentile(step_ms, 90))],
+        "ms_per_step_warm_no_flush": warm_ms,
+        "timing": "HIP events per step after a 1 GiB cache flush; plain stream launches"
+                  if not args.no_flush else "HIP events per step, no flush; plain stream launches",
+        "roofline": {"bound": "hbm", "kernel": d_sym, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": committed_traffic(wl.name, d_sym),
+                     "algorithmic_bytes_per_launch": d_bytes, "avg_launch_ms": d_ms},
+        "wall_s_timed_loop": wall,
+    }
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

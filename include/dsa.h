@@ -1,0 +1,216 @@
+/*
+ * dsa.h — C ABI of the MI355X (gfx950) sparse-attention decode library.
+ *
+ * The library computes the three device steps of DeepSeek-style sparse
+ * attention over a paged latent KV cache, as GLM-5.2 uses it:
+ *
+ *   1. dsa_indexer_scores — lightning-indexer scores of every causal past
+ *      token ("vLLM Inference Path: GLM-5.2 as an Example", section "DSA
+ *      Indexer"; "Making GLM-5.2 Sparse on TPUs", section "Separate the
+ *      indexer from the attention it controls"):
+ *          I[t, s] = sum_j w[t, j] * ReLU(q_idx[t, j, :] . k_idx[s, :]),  s <= t
+ *   2. dsa_topk — the k best token positions per query row ("GLM-5.2 on vLLM
+ *      Ascend: Request-to-Backend Inference Path", section "8. The SFA
+ *      backend, step by step": the operator asks for 2,048 positions and the
+ *      indexer selects tokens, not blocks);
+ *   3. dsa_sparse_mla_fwd — absorbed MLA attention over only the selected
+ *      cache rows ("vLLM Inference Path: GLM-5.2 as an Example", sections
+ *      "MLA Projections and KV State" and "Sparse MLA Attention"; "Making
+ *      GLM-5.2 Sparse on TPUs", section "Separate the indexer from the
+ *      attention it controls").
+ *
+ * IndexShare ("GLM-5.2 on vLLM Ascend ...", section "7. GLM-5.2
+ * shared-indexer construction") is the caller passing one `indices` buffer to
+ * several dsa_sparse_mla_fwd calls, one per layer.
+ *
+ * Conventions common to every call
+ * --------------------------------
+ * - Every pointer argument is a DEVICE pointer unless its comment says host.
+ *   Struct arguments themselves (dsa_batch, dsa_paged_cache) live on the host
+ *   and are only read during the call.
+ * - The caller owns every buffer: inputs, outputs, workspace and stream. The
+ *   library never allocates or frees device memory and never synchronizes.
+ *   All work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *   and is complete when that stream is.
+ * - Errors are status codes. All host-visible arguments are validated before
+ *   anything is enqueued; on an error nothing is enqueued and no output is
+ *   touched. No call aborts or throws across the ABI.
+ * - Device-resident metadata (lengths, block tables, indices) is trusted to
+ *   be in range, but clamped so that malformed values never make a kernel
+ *   read or write outside the buffers described here: page ids are clamped
+ *   to [0, num_pages), logical pages past a sequence's length are never read,
+ *   rows with zero queries are empty, and indices outside [0, t] are treated
+ *   as padding. Malformed metadata thus gives wrong but memory-safe results.
+ * - Calls on different streams may run concurrently; the library keeps no
+ *   mutable state. A workspace must not be shared by calls that may overlap.
+ *
+ * Row positions. Query rows are flattened over the batch: row r = cu_q[b] + i
+ * (0 <= i < q_b = cu_q[b+1] - cu_q[b]) is the token at absolute position
+ * t_r = seq_lens[b] - q_b + i, where seq_lens[b] counts this step's q_b new
+ * tokens ("Making GLM-5.2 Sparse on TPUs", section "Pack requests and reuse
+ * prefixes": causality uses prefix length plus local offset). Row r may use
+ * positions 0..t_r of sequence b, its own position included (its key is
+ * written to the cache before selection).
+ *
+ * Paging. Logical position s of sequence b lives in physical page
+ * block_table[b * bt_stride + s / page_size], slot s % page_size. One block
+ * table serves the indexer-key cache and every layer's latent cache; the
+ * caches themselves are separate buffers.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  DSA_ERR_SHAPE = 2,       /* a size, stride or bound is out of range or inconsistent */
+  DSA_ERR_DTYPE = 3,       /* an element type is not allowed for this argument */
+  DSA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the size query returns */
+  DSA_ERR_UNSUPPORTED = 5, /* a valid combination this build has no kernel for */
+  DSA_ERR_LAUNCH = 6       /* the HIP runtime rejected a kernel launch */
+} dsa_status;
+
+typedef enum {
+  DSA_F32 = 0,      /* IEEE binary32 */
+  DSA_BF16 = 1,     /* bfloat16 */
+  DSA_FP8_E4M3 = 2  /* OCP FP8 E4M3FN: bias 7, no infinities, S.1111.111 = NaN */
+} dsa_dtype;
+
+/* Packed batch metadata, shared by all three calls. The struct is a host
+ * object; the arrays it points to are device arrays. */
+typedef struct {
+  const int32_t *block_table; /* device [batch, bt_stride]: physical page ids */
+  const int32_t *seq_lens;    /* device [batch]: KV length L_b incl. this step's queries */
+  const int32_t *cu_q;        /* device [batch + 1]: query-row offsets, cu_q[0] = 0, non-decreasing */
+  int32_t batch;              /* number of sequences, >= 0 */
+  int32_t bt_stride;          /* block-table row stride in entries, >= ceil(max_seq_len / page_size) */
+  int32_t total_q;            /* host copy of cu_q[batch]: number of query rows T */
+  int32_t max_seq_len;        /* host bound: >= every seq_lens[b] */
+  int32_t max_q;              /* host bound: >= every q_b; 0 < max_q <= total_q unless total_q = 0 */
+} dsa_batch;
+
+/* One paged cache: [num_pages, page_size, row_elems] elements of `dtype`,
+ * rows contiguous. For DSA_FP8_E4M3 `scale` holds one fp32 dequantisation
+ * factor per token, [num_pages, page_size], and the stored key is
+ * scale * e4m3(byte) ("GLM-5.2 on vLLM Ascend ...", section "7. GLM-5.2
+ * shared-indexer construction": FP8 e4m3 keys carry FP32 scales). */
+typedef struct {
+  const void *data;   /* device */
+  const float *scale; /* device [num_pages, page_size]; required for fp8, else ignored */
+  int64_t num_pages;  /* > 0 */
+  int32_t page_size;  /* tokens per page, > 0 */
+  int32_t row_elems;  /* elements per token row (the row stride), > 0 */
+  int32_t dtype;      /* dsa_dtype */
+} dsa_paged_cache;
+
+/* Stable, human-readable name of a status code (a static string). */
+const char *dsa_status_str(dsa_status status);
+
+/* DSA_ABI_VERSION of the built library. */
+int32_t dsa_abi_version(void);
+
+/*
+ * Lightning-indexer scores ("vLLM Inference Path: GLM-5.2 as an Example",
+ * section "DSA Indexer"; "Making GLM-5.2 Sparse on TPUs", section "Separate
+ * the indexer from the attention it controls").
+ *
+ * For every query row r and every position s in [0, t_r]:
+ *   scores[r * ld_scores + s] = sum_j w[r, j] * ReLU(sum_d q_idx[r, j, d] * k(s)[d])
+ * where k(s) is the key row of position s (times its scale for fp8 keys).
+ * Accumulation is fp32. Entries s > t_r of a row are not written.
+ *
+ *   q_idx   device [total_q, n_heads, head_dim], element type q_dtype (F32 or BF16)
+ *   w       device [total_q, n_heads] fp32 per-head weights
+ *   keys    paged key cache, row_elems == head_dim, dtype F32, BF16 or FP8_E4M3;
+ *           F32 queries need F32 keys
+ *   scores  device [total_q, ld_scores] fp32 output; ld_scores >= max_seq_len
+ *
+ * Errors: DSA_ERR_NULL for a NULL batch, keys, q_idx, w, scores, key data,
+ * fp8 scale, or (with total_q > 0) NULL metadata arrays; DSA_ERR_SHAPE for
+ * non-positive heads/dims/page size, row_elems != head_dim, ld_scores <
+ * max_seq_len, or inconsistent batch bounds; DSA_ERR_DTYPE for unsupported
+ * element types; DSA_ERR_LAUNCH if the runtime rejects the launch.
+ */
+dsa_status dsa_indexer_scores(const dsa_batch *batch, const void *q_idx, int32_t q_dtype,
+                              const float *w, int32_t n_heads, int32_t head_dim,
+                              const dsa_paged_cache *keys, float *scores, int64_t ld_scores,
+                              void *stream);
+
+/* Bytes of workspace dsa_topk needs for these host bounds (0 if none). */
+size_t dsa_topk_workspace_size(int32_t total_q, int32_t max_seq_len, int32_t k);
+
+/*
+ * Per-row top-k of the indexer scores ("GLM-5.2 on vLLM Ascend ...", section
+ * "8. The SFA backend, step by step"; "vLLM Inference Path: GLM-5.2 as an
+ * Example", section "DSA Indexer").
+ *
+ * For row r with n = t_r + 1 candidates (reads scores[r * ld_scores + s] for
+ * s < n only) keeps m = min(k, n) positions: the largest scores, equal scores
+ * ordered by lower position first, -0.0 equal to +0.0. Scores must not be
+ * NaN (NaN ordering is unspecified). indices[r * k + 0 .. m-1] receives the
+ * kept positions in ascending order and indices[r * k + m .. k-1] = -1.
+ * Every entry of indices[total_q, k] is written.
+ *
+ *   scores    device [total_q, ld_scores] fp32, as written by dsa_indexer_scores
+ *   indices   device [total_q, k] int32 output
+ *   workspace device, >= dsa_topk_workspace_size(total_q, max_seq_len, k) bytes
+ *             (may be NULL when that size is 0)
+ *
+ * Errors: DSA_ERR_NULL, DSA_ERR_SHAPE (k < 1, ld_scores < max_seq_len, bad
+ * bounds), DSA_ERR_WORKSPACE, DSA_ERR_LAUNCH.
+ */
+dsa_status dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld_scores, int32_t k,
+                    int32_t *indices, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace dsa_sparse_mla_fwd needs for these host bounds. */
+size_t dsa_sparse_mla_workspace_size(int32_t total_q, int32_t n_heads, int32_t d_latent,
+                                     int32_t k);
+
+/*
+ * Absorbed sparse MLA attention over the selected rows ("vLLM Inference
+ * Path: GLM-5.2 as an Example", sections "MLA Projections and KV State" and
+ * "Sparse MLA Attention"; "Making GLM-5.2 Sparse on TPUs", section "Separate
+ * the indexer from the attention it controls").
+ *
+ * Each cache row is [latent (d_latent) | RoPE key (d_rope)]; each query row
+ * holds n_heads absorbed queries of the same width. For row r, head h and the
+ * selected positions S_r = { indices[r * k + i] : 0 <= indices[r*k+i] <= t_r }:
+ *   l_s      = scale * q[r, h, :] . row(s)                 (all d_latent + d_rope dims)
+ *   out[r,h] = sum_{s in S_r} softmax_s(l) * row(s)[0 : d_latent]
+ *   lse[r,h] = log sum_{s in S_r} exp(l_s)                  (natural log)
+ * Rows with no selected position get out = 0 and lse = -inf. A position
+ * listed twice counts twice. The scale is passed explicitly (the pages tie it
+ * to 1/sqrt(192 + 64), not to the absorbed width). Accumulation is fp32.
+ *
+ *   q        device [total_q, n_heads, d_latent + d_rope], element type q_dtype
+ *   kv       paged latent cache, row_elems == d_latent + d_rope, dtype == q_dtype
+ *            (F32 or BF16)
+ *   indices  device [total_q, k] int32, e.g. from dsa_topk
+ *   out      device [total_q, n_heads, d_latent] fp32 output (fully written)
+ *   lse      device [total_q, n_heads] fp32 output, or NULL
+ *   workspace device, >= dsa_sparse_mla_workspace_size(total_q, n_heads, d_latent, k)
+ *
+ * Errors: DSA_ERR_NULL (including a NULL `indices`: a layer that has neither
+ * its own nor a shared top-k buffer is rejected), DSA_ERR_SHAPE, DSA_ERR_DTYPE,
+ * DSA_ERR_WORKSPACE, DSA_ERR_LAUNCH.
+ */
+dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_dtype,
+                              int32_t n_heads, int32_t d_latent, int32_t d_rope,
+                              const dsa_paged_cache *kv, const int32_t *indices, int32_t k,
+                              float scale, float *out, float *lse, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

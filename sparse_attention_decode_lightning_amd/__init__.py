@@ -1,0 +1,179 @@
+"""MI355X sparse-attention decode: lightning indexer -> top-k -> sparse MLA.
+
+Thin torch-facing binding of the C-ABI library ``libdsa.so`` (see
+``include/dsa.h``). PyTorch only supplies device memory and the current
+stream; every step runs in the library's HIP kernels. Each wrapper checks
+dtypes, shapes, devices and contiguity, passes raw pointers, and raises
+:class:`DSAError` on a non-zero status.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import (  # noqa: F401
+    DSA_BF16,
+    DSA_F32,
+    DSA_FP8_E4M3,
+    DSAError,
+    DsaBatch,
+    DsaPagedCache,
+    check,
+    lib,
+    status_str,
+)
+
+__all__ = [
+    "Batch", "PagedCache", "DSAError", "indexer_scores", "topk", "sparse_mla_fwd",
+    "topk_workspace_size", "sparse_mla_workspace_size", "abi_version",
+]
+
+_DT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.uint8: DSA_FP8_E4M3,
+       torch.float8_e4m3fn: DSA_FP8_E4M3}
+
+
+def abi_version() -> int:
+    return int(lib.dsa_abi_version())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+@dataclass
+class Batch:
+    """Packed batch metadata: device arrays plus their host-side bounds."""
+
+    block_table: torch.Tensor  # int32 [B, bt_stride]
+    seq_lens: torch.Tensor  # int32 [B]
+    cu_q: torch.Tensor  # int32 [B + 1]
+    total_q: int
+    max_seq_len: int
+    max_q: int
+
+    def c(self) -> DsaBatch:
+        return DsaBatch(
+            _dev(self.block_table, "block_table", torch.int32),
+            _dev(self.seq_lens, "seq_lens", torch.int32),
+            _dev(self.cu_q, "cu_q", torch.int32),
+            int(self.seq_lens.shape[0]), int(self.block_table.shape[1]), int(self.total_q),
+            int(self.max_seq_len), int(self.max_q))
+
+
+@dataclass
+class PagedCache:
+    """A paged cache [num_pages, page_size, row] (+ fp32 scales [num_pages, page_size] for e4m3)."""
+
+    data: torch.Tensor
+    scale: Optional[torch.Tensor] = None
+
+    def c(self) -> DsaPagedCache:
+        if self.data.dim() != 3:
+            raise ValueError("cache must be [num_pages, page_size, row_elems]")
+        dt = _DT.get(self.data.dtype)
+        if dt is None:
+            raise TypeError(f"unsupported cache dtype {self.data.dtype}")
+        sp = 0
+        if dt == DSA_FP8_E4M3:
+            if self.scale is None:
+                raise ValueError("e4m3 cache needs per-token fp32 scales")
+            if tuple(self.scale.shape) != tuple(self.data.shape[:2]):
+                raise ValueError("scale must be [num_pages, page_size]")
+            sp = _dev(self.scale, "scale", torch.float32)
+        n, p, r = self.data.shape
+        return DsaPagedCache(_dev(self.data, "cache"), sp, n, p, r, dt)
+
+
+def indexer_scores(batch: Batch, q_idx: torch.Tensor, w: torch.Tensor, keys: PagedCache,
+                   scores: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """I[r, s] = sum_j w[r, j] ReLU(q_idx[r, j] . k(s)) for s <= t_r; [T, ld] fp32 (rest untouched)."""
+    T, H, D = q_idx.shape
+    qd = _DT.get(q_idx.dtype)
+    if qd not in (DSA_F32, DSA_BF16):
+        raise TypeError("q_idx must be float32 or bfloat16")
+    if tuple(w.shape) != (T, H):
+        raise ValueError("w must be [T, n_heads]")
+    if scores is None:
+        scores = torch.empty((T, max(1, batch.max_seq_len)), dtype=torch.float32,
+                             device=q_idx.device)
+    if scores.dim() != 2 or scores.shape[0] != T:
+        raise ValueError("scores must be [T, ld]")
+    b, kc = batch.c(), keys.c()
+    check(lib.dsa_indexer_scores(ctypes.byref(b), _dev(q_idx, "q_idx"), qd,
+                                 _dev(w, "w", torch.float32), H, D, ctypes.byref(kc),
+                                 _dev(scores, "scores", torch.float32), scores.shape[1],
+                                 _stream(q_idx.device)), "dsa_indexer_scores")
+    return scores
+
+
+def topk_workspace_size(total_q: int, max_seq_len: int, k: int) -> int:
+    return int(lib.dsa_topk_workspace_size(total_q, max_seq_len, k))
+
+
+def topk(batch: Batch, scores: torch.Tensor, k: int, indices: Optional[torch.Tensor] = None,
+         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """[T, k] int32: the min(k, t_r + 1) best positions per row, ascending, then -1."""
+    T = scores.shape[0]
+    if indices is None:
+        indices = torch.empty((T, k), dtype=torch.int32, device=scores.device)
+    if tuple(indices.shape) != (T, k):
+        raise ValueError("indices must be [T, k]")
+    need = topk_workspace_size(batch.total_q, batch.max_seq_len, k)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    wp = 0 if workspace is None else _dev(workspace, "workspace")
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    b = batch.c()
+    check(lib.dsa_topk(ctypes.byref(b), _dev(scores, "scores", torch.float32), scores.shape[1], k,
+                       _dev(indices, "indices", torch.int32), wp, wb, _stream(scores.device)),
+          "dsa_topk")
+    return indices
+
+
+def sparse_mla_workspace_size(total_q: int, n_heads: int, d_latent: int, k: int) -> int:
+    return int(lib.dsa_sparse_mla_workspace_size(total_q, n_heads, d_latent, k))
+
+
+def sparse_mla_fwd(batch: Batch, q: torch.Tensor, kv: PagedCache, indices: torch.Tensor,
+                   d_latent: int, scale: float, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Absorbed sparse MLA: out [T, H, d_latent] fp32 and lse [T, H] fp32 (natural log)."""
+    T, H, D = q.shape
+    qd = _DT.get(q.dtype)
+    if qd not in (DSA_F32, DSA_BF16):
+        raise TypeError("q must be float32 or bfloat16")
+    d_rope = D - d_latent
+    k = indices.shape[1]
+    if out is None:
+        out = torch.empty((T, H, d_latent), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    need = sparse_mla_workspace_size(batch.total_q, H, d_latent, k)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wp = 0 if workspace is None else _dev(workspace, "workspace")
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    b, kc = batch.c(), kv.c()
+    check(lib.dsa_sparse_mla_fwd(ctypes.byref(b), _dev(q, "q"), qd, H, d_latent, d_rope,
+                                 ctypes.byref(kc), _dev(indices, "indices", torch.int32), k,
+                                 float(scale), _dev(out, "out", torch.float32),
+                                 0 if lse is None else _dev(lse, "lse", torch.float32), wp, wb,
+                                 _stream(q.device)), "dsa_sparse_mla_fwd")
+    return out, lse

@@ -1,0 +1,158 @@
+// C ABI of the sparse-attention decode library: argument validation, then a
+// launch on the caller's stream. Validation touches no HIP API, so every
+// error path can be exercised without a GPU; nothing is enqueued on error.
+#include <math.h>
+
+#include "dsa_internal.h"
+
+namespace {
+
+using dsa::BatchArgs;
+using dsa::CacheArgs;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+dsa_status check_batch(const dsa_batch *bt, BatchArgs *out) {
+  if (bt == nullptr) return DSA_ERR_NULL;
+  if (bt->batch < 0 || bt->total_q < 0 || bt->max_seq_len < 0 || bt->max_q < 0 ||
+      bt->bt_stride < 0)
+    return DSA_ERR_SHAPE;
+  if (bt->total_q > 0) {
+    if (bt->block_table == nullptr || bt->seq_lens == nullptr || bt->cu_q == nullptr)
+      return DSA_ERR_NULL;
+    if (!aligned(bt->block_table, 4) || !aligned(bt->seq_lens, 4) || !aligned(bt->cu_q, 4))
+      return DSA_ERR_SHAPE;
+    if (bt->batch < 1 || bt->max_q < 1 || bt->max_q > bt->total_q || bt->max_seq_len < 1 ||
+        bt->bt_stride < 1)
+      return DSA_ERR_SHAPE;
+  }
+  out->block_table = bt->block_table;
+  out->seq_lens = bt->seq_lens;
+  out->cu_q = bt->cu_q;
+  out->batch = bt->batch;
+  out->bt_stride = bt->bt_stride;
+  out->total_q = bt->total_q;
+  out->max_seq_len = bt->max_seq_len;
+  out->max_q = bt->max_q;
+  return DSA_OK;
+}
+
+dsa_status check_cache(const dsa_paged_cache *c, const BatchArgs &bt, CacheArgs *out) {
+  if (c == nullptr || c->data == nullptr) return DSA_ERR_NULL;
+  if (c->dtype != DSA_F32 && c->dtype != DSA_BF16 && c->dtype != DSA_FP8_E4M3)
+    return DSA_ERR_DTYPE;
+  if (c->dtype == DSA_FP8_E4M3 && c->scale == nullptr) return DSA_ERR_NULL;
+  if (c->num_pages < 1 || c->page_size < 1 || c->row_elems < 1) return DSA_ERR_SHAPE;
+  if (!aligned(c->data, 16) || (c->dtype == DSA_FP8_E4M3 && !aligned(c->scale, 4)))
+    return DSA_ERR_SHAPE;
+  if (bt.total_q > 0 && (int64_t)bt.bt_stride < ceil_div(bt.max_seq_len, c->page_size))
+    return DSA_ERR_SHAPE;
+  out->data = c->data;
+  out->scale = c->dtype == DSA_FP8_E4M3 ? c->scale : nullptr;
+  out->num_pages = c->num_pages;
+  out->page_size = c->page_size;
+  out->row_elems = c->row_elems;
+  out->dtype = c->dtype;
+  return DSA_OK;
+}
+
+dsa_status launch_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char *dsa_status_str(dsa_status status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_NULL: return "DSA_ERR_NULL: a required pointer is NULL";
+    case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE: a size, stride, bound or alignment is invalid";
+    case DSA_ERR_DTYPE: return "DSA_ERR_DTYPE: element type not allowed here";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: no kernel for this combination";
+    case DSA_ERR_LAUNCH: return "DSA_ERR_LAUNCH: the HIP runtime rejected a launch";
+  }
+  return "DSA_ERR_UNKNOWN";
+}
+
+int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+dsa_status dsa_indexer_scores(const dsa_batch *batch, const void *q_idx, int32_t q_dtype,
+                              const float *w, int32_t n_heads, int32_t head_dim,
+                              const dsa_paged_cache *keys, float *scores, int64_t ld_scores,
+                              void *stream) {
+  BatchArgs bt;
+  CacheArgs kc;
+  dsa_status st = check_batch(batch, &bt);
+  if (st != DSA_OK) return st;
+  if (keys == nullptr || q_idx == nullptr || w == nullptr || scores == nullptr) return DSA_ERR_NULL;
+  st = check_cache(keys, bt, &kc);
+  if (st != DSA_OK) return st;
+  if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (q_dtype == DSA_F32 && kc.dtype != DSA_F32) return DSA_ERR_DTYPE;
+  if (q_dtype == DSA_BF16 && kc.dtype == DSA_F32) return DSA_ERR_DTYPE;
+  if (n_heads < 1 || head_dim < 1 || kc.row_elems != head_dim) return DSA_ERR_SHAPE;
+  if (ld_scores < bt.max_seq_len || ld_scores < 1) return DSA_ERR_SHAPE;
+  if (!aligned(q_idx, 16) || !aligned(w, 4) || !aligned(scores, 4)) return DSA_ERR_SHAPE;
+  return launch_status(dsa::launch_indexer_scores(bt, q_idx, q_dtype, w, n_heads, head_dim, kc,
+                                                  scores, ld_scores,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+size_t dsa_topk_workspace_size(int32_t total_q, int32_t max_seq_len, int32_t k) {
+  return dsa::topk_workspace_bytes(total_q, max_seq_len, k);
+}
+
+dsa_status dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld_scores, int32_t k,
+                    int32_t *indices, void *workspace, size_t workspace_bytes, void *stream) {
+  BatchArgs bt;
+  dsa_status st = check_batch(batch, &bt);
+  if (st != DSA_OK) return st;
+  if (scores == nullptr || indices == nullptr) return DSA_ERR_NULL;
+  if (k < 1 || ld_scores < bt.max_seq_len || ld_scores < 1) return DSA_ERR_SHAPE;
+  if (!aligned(scores, 4) || !aligned(indices, 4)) return DSA_ERR_SHAPE;
+  const size_t need = dsa::topk_workspace_bytes(bt.total_q, bt.max_seq_len, k);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+  return launch_status(dsa::launch_topk(bt, scores, ld_scores, k, indices, workspace,
+                                        workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+size_t dsa_sparse_mla_workspace_size(int32_t total_q, int32_t n_heads, int32_t d_latent,
+                                     int32_t k) {
+  if (total_q < 1 || n_heads < 1 || d_latent < 1 || k < 1) return 0;
+  return dsa::mla_workspace_bytes(total_q, n_heads, d_latent, k);
+}
+
+dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_dtype,
+                              int32_t n_heads, int32_t d_latent, int32_t d_rope,
+                              const dsa_paged_cache *kv, const int32_t *indices, int32_t k,
+                              float scale, float *out, float *lse, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  BatchArgs bt;
+  CacheArgs kc;
+  dsa_status st = check_batch(batch, &bt);
+  if (st != DSA_OK) return st;
+  if (kv == nullptr || q == nullptr || indices == nullptr || out == nullptr) return DSA_ERR_NULL;
+  st = check_cache(kv, bt, &kc);
+  if (st != DSA_OK) return st;
+  if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (kc.dtype != q_dtype) return DSA_ERR_DTYPE;
+  if (n_heads < 1 || d_latent < 1 || d_rope < 0 || k < 1) return DSA_ERR_SHAPE;
+  if ((int64_t)kc.row_elems != (int64_t)d_latent + d_rope) return DSA_ERR_SHAPE;
+  if (!isfinite(scale)) return DSA_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(indices, 4) || !aligned(out, 16) ||
+      (lse != nullptr && !aligned(lse, 4)))
+    return DSA_ERR_SHAPE;
+  if (d_latent > 1024 && !(q_dtype == DSA_BF16 && n_heads == 64 && d_latent == 512 && d_rope == 64))
+    return DSA_ERR_UNSUPPORTED;
+  const size_t need = dsa::mla_workspace_bytes(bt.total_q, n_heads, d_latent, k);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+    return DSA_ERR_WORKSPACE;
+  return launch_status(dsa::launch_sparse_mla(bt, q, q_dtype, n_heads, d_latent, d_rope, kc,
+                                              indices, k, scale, out, lse, workspace,
+                                              workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Device-side helpers shared by the gfx950 kernels: element conversions,
+// MFMA fragment types, wave reductions and paged-cache addressing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs here are finite probabilities).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// OCP E4M3FN byte -> bf16 bits, exact (every e4m3fn value is a bf16 value).
+// Normal codes (exponent field e >= 1): 2^(e-7) * (1 + m/8) -> bf16 exponent
+// e + 120 with the three mantissa bits on top; subnormals m * 2^-9 go through
+// an exact int -> float conversion; S.1111.111 is NaN.
+__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t byte) {
+  uint32_t sign = (byte & 0x80u) << 8;
+  uint32_t em = byte & 0x7Fu;
+  uint32_t normal = (em << 4) + (120u << 7);
+  uint32_t sub = __float_as_uint((float)em * 0.001953125f) >> 16;
+  uint32_t mag = em >= 8u ? normal : sub;
+  mag = em == 0x7Fu ? 0x7FC0u : mag;
+  return sign | mag;
+}
+
+// Four e4m3 bytes packed in a dword -> two dwords of bf16 pairs (low byte first).
+__device__ __forceinline__ u32x2_t e4m3x4_to_bf16x4(uint32_t w) {
+  u32x2_t r;
+  r.x = e4m3_to_bf16(w & 0xFFu) | (e4m3_to_bf16((w >> 8) & 0xFFu) << 16);
+  r.y = e4m3_to_bf16((w >> 16) & 0xFFu) | (e4m3_to_bf16(w >> 24) << 16);
+  return r;
+}
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4_t ldg16(const void *p) {
+  return *reinterpret_cast<const u32x4_t *>(p);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Sequence of a flattened query row: the largest b with cu_q[b] <= row.
+// cu_q is non-decreasing, so cu_q[b] <= row < cu_q[b + 1] for the result.
+__device__ __forceinline__ int find_seq(const int32_t *cu_q, int batch, int row) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct RowInfo {
+  int b;  // sequence of the row
+  int t;  // absolute position of the row; -1 if the metadata leaves it none
+};
+
+// Sequence and causal position of a flattened query row, with every value
+// clamped so malformed metadata can never index past the caller's buffers:
+// q offsets into [0, total_q], lengths into [0, max_seq_len], t <= L - 1.
+__device__ __forceinline__ RowInfo row_info(const int32_t *cu_q, const int32_t *seq_lens,
+                                            int batch, int total_q, int max_seq_len, int row) {
+  RowInfo ri;
+  ri.b = find_seq(cu_q, batch, row);
+  const int q0 = min(max(cu_q[ri.b], 0), total_q);
+  const int q1 = min(max(cu_q[ri.b + 1], q0), total_q);
+  const int L = min(max(seq_lens[ri.b], 0), max_seq_len);
+  const int t = L - (q1 - q0) + (row - q0);
+  ri.t = (row < q0 || row >= q1) ? -1 : min(t, L - 1);
+  ri.t = ri.t < -1 ? -1 : ri.t;
+  return ri;
+}
+
+// Element offset of token `pos` of sequence `b` in a paged cache, with the
+// physical page id clamped into the pool so malformed tables stay in bounds.
+__device__ __forceinline__ int64_t paged_row(const int32_t *block_table, int64_t bt_stride, int b,
+                                             int pos, int page_size, int64_t num_pages) {
+  int64_t page = block_table[(int64_t)b * bt_stride + pos / page_size];
+  page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+  return page * page_size + pos % page_size;
+}
+
+}  // namespace dsa

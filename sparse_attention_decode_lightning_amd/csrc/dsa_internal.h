@@ -1,0 +1,49 @@
+// Internal launcher interface between the C ABI (dsa_api.cpp) and the kernel
+// translation units. Arguments have already been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+struct BatchArgs {
+  const int32_t *block_table;
+  const int32_t *seq_lens;
+  const int32_t *cu_q;
+  int32_t batch;
+  int64_t bt_stride;
+  int32_t total_q;
+  int32_t max_seq_len;
+  int32_t max_q;
+};
+
+struct CacheArgs {
+  const void *data;
+  const float *scale;
+  int64_t num_pages;
+  int32_t page_size;
+  int32_t row_elems;
+  int32_t dtype;
+};
+
+hipError_t launch_indexer_scores(const BatchArgs &bt, const void *q_idx, int32_t q_dtype,
+                                 const float *w, int32_t n_heads, int32_t head_dim,
+                                 const CacheArgs &keys, float *scores, int64_t ld_scores,
+                                 hipStream_t stream);
+
+size_t topk_workspace_bytes(int32_t total_q, int32_t max_seq_len, int32_t k);
+hipError_t launch_topk(const BatchArgs &bt, const float *scores, int64_t ld_scores, int32_t k,
+                       int32_t *indices, void *workspace, size_t ws_bytes, hipStream_t stream);
+
+int mla_num_splits(int32_t total_q, int32_t n_heads, int32_t d_latent, int32_t k);
+size_t mla_workspace_bytes(int32_t total_q, int32_t n_heads, int32_t d_latent, int32_t k);
+hipError_t launch_sparse_mla(const BatchArgs &bt, const void *q, int32_t q_dtype, int32_t n_heads,
+                             int32_t d_latent, int32_t d_rope, const CacheArgs &kv,
+                             const int32_t *indices, int32_t k, float scale, float *out, float *lse,
+                             void *workspace, size_t ws_bytes, hipStream_t stream);
+
+}  // namespace dsa

@@ -15,3 +15,13 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def _ensure_built():
+    lib = os.path.join(ROOT, "sparse_attention_decode_lightning_amd", "libdsa.so")
+    if not os.path.exists(lib):
+        from sparse_attention_decode_lightning_amd import build as _b
+        _b.build(verbose=False)
+
+
+_ensure_built()

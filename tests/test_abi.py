@@ -1,0 +1,137 @@
+"""The C-ABI library: it loads, exports what include/dsa.h declares, lays out its
+structs as C does, and rejects bad arguments with status codes before touching
+the GPU (CPU only; no kernel is launched here)."""
+
+import ctypes
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+from sparse_attention_decode_lightning_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000  # an aligned address that validation rejects before any use
+
+
+def test_every_declared_symbol_is_exported():
+    names = L.declared_functions()
+    assert set(names) >= {"dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_fwd",
+                          "dsa_topk_workspace_size", "dsa_sparse_mla_workspace_size",
+                          "dsa_status_str", "dsa_abi_version"}
+    for n in names:
+        assert hasattr(L.lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(names) <= exported
+
+
+def test_abi_version_and_status_strings():
+    assert L.lib.dsa_abi_version() == 1
+    for code, name in L.STATUS_NAMES.items():
+        assert L.status_str(code).startswith(name)
+
+
+def test_struct_layout_matches_c():
+    src = r'''
+#include <stddef.h>
+#include <stdio.h>
+#include "dsa.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(dsa_batch), offsetof(dsa_batch, batch),
+         offsetof(dsa_batch, max_q), sizeof(dsa_paged_cache),
+         offsetof(dsa_paged_cache, num_pages), offsetof(dsa_paged_cache, dtype));
+  return 0;
+}
+'''
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "l.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "l")
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), c, "-o", exe],
+                       check=True)
+        got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
+                                              check=True).stdout.split()]
+    assert got == [ctypes.sizeof(L.DsaBatch), L.DsaBatch.batch.offset, L.DsaBatch.max_q.offset,
+                   ctypes.sizeof(L.DsaPagedCache), L.DsaPagedCache.num_pages.offset,
+                   L.DsaPagedCache.dtype.offset]
+
+
+def _batch(**kw):
+    d = dict(block_table=FAKE, seq_lens=FAKE, cu_q=FAKE, batch=2, bt_stride=4, total_q=2,
+             max_seq_len=200, max_q=1)
+    d.update(kw)
+    return L.DsaBatch(**d)
+
+
+def _cache(**kw):
+    d = dict(data=FAKE, scale=FAKE, num_pages=10, page_size=64, row_elems=128, dtype=L.DSA_BF16)
+    d.update(kw)
+    return L.DsaPagedCache(**d)
+
+
+def _idx(b=None, q=FAKE, qd=L.DSA_BF16, w=FAKE, H=32, D=128, c=None, s=FAKE, ld=256):
+    b = _batch() if b is None else b
+    c = _cache() if c is None else c
+    return L.lib.dsa_indexer_scores(ctypes.byref(b) if b is not False else None, q, qd, w, H, D,
+                                    ctypes.byref(c) if c is not False else None, s, ld, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=False), 1), (dict(q=None), 1), (dict(w=None), 1), (dict(s=None), 1),
+    (dict(c=False), 1), (dict(c=_cache(data=None)), 1),
+    (dict(c=_cache(dtype=L.DSA_FP8_E4M3, row_elems=128, scale=None)), 1),
+    (dict(b=_batch(seq_lens=None)), 1),
+    (dict(ld=199), 2), (dict(H=0), 2), (dict(D=64), 2), (dict(c=_cache(page_size=0)), 2),
+    (dict(c=_cache(num_pages=0)), 2), (dict(b=_batch(bt_stride=3)), 2),
+    (dict(b=_batch(max_q=3)), 2), (dict(b=_batch(batch=-1)), 2), (dict(q=FAKE + 8), 2),
+    (dict(qd=7), 3), (dict(c=_cache(dtype=9)), 3), (dict(qd=L.DSA_F32), 3),
+    (dict(c=_cache(dtype=L.DSA_F32)), 3),
+])
+def test_indexer_rejects_bad_arguments(kw, code):
+    assert _idx(**kw) == code
+
+
+def _topk(b=None, s=FAKE, ld=256, k=64, idx=FAKE):
+    b = _batch() if b is None else b
+    return L.lib.dsa_topk(ctypes.byref(b) if b is not False else None, s, ld, k, idx, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=False), 1), (dict(s=None), 1), (dict(idx=None), 1),
+    (dict(k=0), 2), (dict(ld=100), 2), (dict(idx=FAKE + 2), 2), (dict(b=_batch(total_q=-1)), 2),
+])
+def test_topk_rejects_bad_arguments(kw, code):
+    assert _topk(**kw) == code
+
+
+def _mla(b=None, q=FAKE, qd=L.DSA_BF16, H=64, DL=512, DR=64, c=None, idx=FAKE, k=2048,
+         scale=0.0625, out=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 40):
+    b = _batch() if b is None else b
+    c = _cache(row_elems=576) if c is None else c
+    return L.lib.dsa_sparse_mla_fwd(ctypes.byref(b) if b is not False else None, q, qd, H, DL, DR,
+                                    ctypes.byref(c) if c is not False else None, idx, k, scale,
+                                    out, lse, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=False), 1), (dict(q=None), 1), (dict(idx=None), 1), (dict(out=None), 1),
+    (dict(c=False), 1),
+    (dict(DR=32), 2), (dict(k=0), 2), (dict(scale=float("nan")), 2), (dict(H=0), 2),
+    (dict(out=FAKE + 4), 2),
+    (dict(qd=L.DSA_F32), 3), (dict(c=_cache(row_elems=576, dtype=L.DSA_FP8_E4M3)), 3),
+    (dict(ws=None), 4), (dict(wsb=16), 4),
+    (dict(qd=L.DSA_F32, c=_cache(row_elems=2048 + 64, dtype=L.DSA_F32), DL=2048), 5),
+])
+def test_mla_rejects_bad_arguments(kw, code):
+    assert _mla(**kw) == code
+
+
+def test_workspace_sizes_are_pure_functions_of_bounds():
+    assert L.lib.dsa_topk_workspace_size(32, 8192, 2048) == 0
+    s = L.lib.dsa_sparse_mla_workspace_size(32, 64, 512, 2048)
+    assert s > 0 and s == L.lib.dsa_sparse_mla_workspace_size(32, 64, 512, 2048)
+    assert L.lib.dsa_sparse_mla_workspace_size(4096, 64, 512, 2048) == 0
+    assert L.lib.dsa_sparse_mla_workspace_size(0, 64, 512, 2048) == 0

@@ -1,0 +1,133 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Small cases are compared element by element (several tiles and ragged tails,
+every kernel variant); the five full-size workloads run in the launch
+configuration the benchmark times and are compared on sampled rows, with the
+index invariants checked on every row.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from tests import parity as P
+from workloads import WORKLOADS, host_view, make_inputs, small_variant, to_device
+
+pytestmark = pytest.mark.gpu
+
+BF16_DECODE = small_variant("decode_b32_l8k", batch=3, lens=(300, 1000, 2071), topk=256)
+SMALL_CASES = {
+    "tiny_f32": WORKLOADS["tiny"],
+    "bf16_decode_ragged": BF16_DECODE,
+    "fp8_decode_ragged": small_variant("indexshare_b64", batch=4, lens=(2049, 100, 777, 4096),
+                                       topk=512, n_layers=2),
+    "fp8_multiquery": small_variant("verify_b8_l240k", batch=2, lens=(1500, 777), topk=256),
+    "bf16_prefill": small_variant("prefill_q4k_l32k", batch=1, lens=1200, q_per_seq=300,
+                                  topk=256),
+    "edge_lengths": small_variant(BF16_DECODE, batch=4, lens=(5, 1, 70, 64), q_per_seq=(1, 0, 3, 1),
+                                  topk=64),
+    "page_size_1": small_variant(BF16_DECODE, batch=2, lens=(130, 47), page_size=1, topk=32),
+    "page_size_16_k_ge_len": small_variant(BF16_DECODE, batch=2, lens=(200, 333), page_size=16,
+                                           topk=512),
+    "idx64_heads": small_variant(BF16_DECODE, batch=2, lens=(500, 260), idx_heads=64, topk=128),
+    "idx16_heads_multiq": small_variant("verify_b8_l240k", batch=2, lens=(400, 90), q_per_seq=5,
+                                        idx_heads=16, topk=64),
+    "mla_generic_bf16": small_variant(BF16_DECODE, batch=2, lens=(300, 129), mla_heads=16,
+                                      d_latent=128, d_rope=32, topk=100),
+}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("name", list(SMALL_CASES))
+def test_small_case_full_parity(name, dev):
+    wl = SMALL_CASES[name]
+    print(f"[parity] {name}", flush=True)
+    inp_h = make_inputs(wl)
+    inp = to_device(inp_h, dev)
+    host = host_view(inp_h)
+    scores, idx, outs = P.run_gpu(inp)
+    rows = list(range(inp.total_q))
+    ref_scores = P.check_scores(inp, scores, rows, host)
+    P.check_topk_identical(scores, idx, rows, inp, wl.topk)
+    P.check_topk_band(ref_scores, idx, rows, wl.topk)
+    P.check_invariants(inp, idx, wl.topk)
+    for l, (out, lse) in enumerate(outs):
+        P.check_mla(inp, l, idx, out, lse, rows, host)
+
+
+def test_indexshare_layers_reuse_one_topk(dev):
+    """One top-k buffer serves several layers; each layer's output is its own oracle's."""
+    wl = small_variant("indexshare_b64", batch=3, lens=(3000, 2100, 5000), topk=1024, n_layers=3)
+    inp_h = make_inputs(wl)
+    inp = to_device(inp_h, dev)
+    _, idx, outs = P.run_gpu(inp)
+    host = host_view(inp_h)
+    rows = list(range(inp.total_q))
+    for l, (out, lse) in enumerate(outs):
+        P.check_mla(inp, l, idx, out, lse, rows, host)
+    assert not torch.equal(outs[0][0], outs[1][0])
+
+
+def test_block_table_permutation_invariance(dev):
+    """Same logical caches under two different physical page layouts give identical outputs."""
+    wl = small_variant(BF16_DECODE, batch=2, lens=(700, 1300))
+    a_h = make_inputs(wl)
+    b_h = make_inputs(wl.replace(seed=wl.seed))  # same draw
+    pool = a_h.k_cache.shape[0]
+    perm = torch.randperm(pool, generator=torch.Generator().manual_seed(99))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(pool)
+    b_h.block_table = inv[a_h.block_table.long()].to(torch.int32)
+    b_h.k_cache = torch.empty_like(a_h.k_cache)
+    b_h.k_cache[inv] = a_h.k_cache
+    b_h.kv_cache = [torch.empty_like(c) for c in a_h.kv_cache]
+    b_h.kv_cache[0][inv] = a_h.kv_cache[0]
+    sa, ia, oa = P.run_gpu(to_device(a_h, dev))
+    sb, ib, ob = P.run_gpu(to_device(b_h, dev))
+    for r in range(a_h.total_q):
+        t = a_h.seq_lens_host[r] - 1
+        assert torch.equal(sa[r, : t + 1], sb[r, : t + 1])
+    assert torch.equal(ia, ib)
+    assert torch.equal(oa[0][0], ob[0][0])
+
+
+def test_mutated_metadata_is_detected(dev):
+    """Feeding a swapped block-table row must break parity (the comparison is sensitive)."""
+    wl = small_variant(BF16_DECODE, batch=2, lens=(1024, 1024), topk=128)
+    inp_h = make_inputs(wl)
+    bad_h = make_inputs(wl)
+    bad_h.block_table = bad_h.block_table.flip(0).contiguous()
+    scores, _, _ = P.run_gpu(to_device(bad_h, dev))
+    with pytest.raises(AssertionError):
+        P.check_scores(inp_h, scores, [0, 1], host_view(inp_h))
+
+
+FULL = ["decode_b32_l8k", "indexshare_b64", "prefill_q4k_l32k", "verify_b8_l240k"]
+SAMPLE_ROWS = {
+    "decode_b32_l8k": [0, 13, 31],
+    "indexshare_b64": [0, 17, 40, 63],
+    "prefill_q4k_l32k": [0, 1, 777, 2048, 4095],
+    "verify_b8_l240k": [0, 3, 18, 31],
+}
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_parity(name, dev):
+    wl = WORKLOADS[name]
+    print(f"[parity-full] {name}", flush=True)
+    inp = make_inputs(wl, device="cuda")
+    scores, idx, outs = P.run_gpu(inp, canary=False)
+    rows = SAMPLE_ROWS[name]
+    host = host_view(inp, lazy=True)
+    ref = P.check_scores(inp, scores, rows, host)
+    P.check_topk_identical(scores, idx, rows, inp, wl.topk)
+    P.check_topk_band(ref, idx, rows, wl.topk)
+    P.check_invariants(inp, idx, wl.topk)
+    for l, (out, lse) in enumerate(outs):
+        assert torch.isfinite(out).all()
+        P.check_mla(inp, l, idx, out, lse, rows, host)

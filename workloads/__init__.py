@@ -15,4 +15,5 @@ from .gen import (  # noqa: F401
     host_view,
     raw_numpy,
     PagedRows,
+    to_device,
 )

@@ -348,3 +348,13 @@ def host_view(inp: Inputs, lazy: bool = False) -> dict:
         "scale": wl.scale,
         "topk": wl.topk,
     }
+
+
+def to_device(inp: Inputs, device) -> Inputs:
+    """A copy of ``inp`` with every tensor moved to ``device`` (host metadata kept)."""
+    mv = lambda t: None if t is None else t.to(device)  # noqa: E731
+    return dataclasses.replace(
+        inp, seq_lens=mv(inp.seq_lens), q_lens=mv(inp.q_lens), cu_q=mv(inp.cu_q),
+        block_table=mv(inp.block_table), q_idx=mv(inp.q_idx), w=mv(inp.w),
+        k_cache=mv(inp.k_cache), k_scale=mv(inp.k_scale),
+        q_mla=[mv(q) for q in inp.q_mla], kv_cache=[mv(c) for c in inp.kv_cache])
