@@ -6,11 +6,15 @@ top-k -> one sparse-MLA call per layer (the layers share the top-k, as in
 IndexShare). Inputs are seeded synthetic data already resident in HBM.
 
 Timing: W untimed warm-up steps, then K timed steps. Before every timed step a
-1 GiB buffer is overwritten (outside the timed interval) so the 256 MB
-Infinity Cache and the L2s hold none of the step's inputs; each step is timed
+1 GiB buffer is read (outside the timed interval) so the 256 MB Infinity Cache
+and the L2s hold none of the step's inputs; reading (not writing) leaves the
+caches clean, so no write-back of the eviction traffic lands inside the timed
+step. Each step is timed
 with HIP events on the stream the kernels run on, with one extra event between
-consecutive library calls to time each kernel. The whole timed loop is
-bracketed by device synchronizations.
+consecutive library calls on separate (eager) steps to time each kernel. With
+--graph the timed steps are replayed from a captured HIP graph (checked
+bit-exact against the eager step); by default they are eager stream launches. The whole timed loop is bracketed
+by device synchronizations.
 
 Prints one JSON line: throughput in query tokens/s, the dominant kernel's
 achieved algorithmic bandwidth against the HBM peak, and the CPU oracle's
@@ -42,7 +46,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=WORKLOAD_DEFAULT)
-    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache eviction between steps")
+    ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=False,
+                    help="replay the step as a captured HIP graph instead of eager launches")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample (0 = skip)")
     return ap.parse_args()
@@ -164,7 +170,7 @@ def main():
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     tk_bytes = dsa.topk_workspace_size(T, inp.max_seq_len, wl.topk)
     tk_ws = torch.empty(max(tk_bytes, 16), dtype=torch.uint8, device=dev) if tk_bytes else None
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = torch.ones(1 << 27, dtype=torch.int64, device=dev)  # 1 GiB, evicted by reading
     stream = torch.cuda.current_stream(dev)
     n_ev = 3 + wl.n_layers
 
@@ -183,34 +189,62 @@ def main():
             if evs is not None:
                 evs[3 + l].record(stream)
 
+    def evict():
+        if not args.no_flush:
+            flush.sum()
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    ref_out = outs[-1].clone()
+    ref_idx = indices.clone()
 
-    evsets = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-              for _ in range(args.steps)]
+    replay = step
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            outs[-1].zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            if not (torch.equal(outs[-1], ref_out) and torch.equal(indices, ref_idx)):
+                raise RuntimeError("graph replay does not reproduce the eager step")
+        replay = graph.replay
+
+    # per-stage breakdown: eager launches, an event between consecutive calls
+    n_stage = min(args.steps, 10)
+    evsets = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(n_stage)]
+    for i in range(n_stage):
+        evict()
+        step(evsets[i])
+    torch.cuda.synchronize()
+    per = np.array([[evs[j].elapsed_time(evs[j + 1]) for j in range(n_ev - 1)]
+                    for evs in evsets])  # ms, [steps, stages]
+    stage_ms = per.mean(axis=0)
+
+    # timed steps: start/end events only
+    tev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if not args.no_flush:
-            flush.fill_(i & 0xFF)
-        step(evsets[i])
+        evict()
+        tev[i][0].record(stream)
+        replay()
+        tev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    per = np.array([[evs[j].elapsed_time(evs[j + 1]) for j in range(n_ev - 1)]
-                    for evs in evsets])  # ms, [steps, stages]
-    step_ms = per.sum(axis=1)
+    step_ms = np.array([a.elapsed_time(b) for a, b in tev])
     ms = float(np.mean(step_ms))
-    stage_ms = per.mean(axis=0)
 
-    # warm back-to-back figure (no flush), for context
-    torch.cuda.synchronize()
+    # warm back-to-back figure (no eviction), for context
     w0 = torch.cuda.Event(enable_timing=True)
     w1 = torch.cuda.Event(enable_timing=True)
     w0.record(stream)
     for _ in range(args.steps):
-        step()
+        replay()
     w1.record(stream)
     torch.cuda.synchronize()
     warm_ms = w0.elapsed_time(w1) / args.steps
@@ -248,8 +282,10 @@ def main():
         "ms_per_step_p10_p90": [float(np.percentile(step_ms, 10)),
                                 float(np.percentile(step_ms, 90))],
         "ms_per_step_warm_no_flush": warm_ms,
-        "timing": "HIP events per step after a 1 GiB cache flush; plain stream launches"
-                  if not args.no_flush else "HIP events per step, no flush; plain stream launches",
+        "timing": ("HIP events around each step" +
+                   ("" if args.no_flush else " after a 1 GiB read that evicts the caches") +
+                   ("; HIP graph replay of the captured step" if args.graph
+                    else "; plain stream launches")),
         "roofline": {"bound": "hbm", "kernel": d_sym, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": committed_traffic(wl.name, d_sym),

@@ -113,8 +113,10 @@ dsa_status dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld_scor
   if (scores == nullptr || indices == nullptr) return DSA_ERR_NULL;
   if (k < 1 || ld_scores < bt.max_seq_len || ld_scores < 1) return DSA_ERR_SHAPE;
   if (!aligned(scores, 4) || !aligned(indices, 4)) return DSA_ERR_SHAPE;
+  if (!dsa::topk_supported(bt.max_seq_len, k)) return DSA_ERR_UNSUPPORTED;
   const size_t need = dsa::topk_workspace_bytes(bt.total_q, bt.max_seq_len, k);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+    return DSA_ERR_WORKSPACE;
   return launch_status(dsa::launch_topk(bt, scores, ld_scores, k, indices, workspace,
                                         workspace_bytes, static_cast<hipStream_t>(stream)));
 }
@@ -145,8 +147,9 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_d
   if (!aligned(q, 16) || !aligned(indices, 4) || !aligned(out, 16) ||
       (lse != nullptr && !aligned(lse, 4)))
     return DSA_ERR_SHAPE;
-  if (d_latent > 1024 && !(q_dtype == DSA_BF16 && n_heads == 64 && d_latent == 512 && d_rope == 64))
-    return DSA_ERR_UNSUPPORTED;
+  const bool mfma_shape = q_dtype == DSA_BF16 && n_heads == 64 && d_latent == 512 && d_rope == 64;
+  if (!mfma_shape && d_latent > 1024) return DSA_ERR_UNSUPPORTED;
+  if (mfma_shape && k > dsa::mla_max_k()) return DSA_ERR_UNSUPPORTED;
   const size_t need = dsa::mla_workspace_bytes(bt.total_q, n_heads, d_latent, k);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
     return DSA_ERR_WORKSPACE;

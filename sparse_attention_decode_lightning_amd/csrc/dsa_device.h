@@ -56,6 +56,36 @@ __device__ __forceinline__ u32x4_t ldg16(const void *p) {
   return *reinterpret_cast<const u32x4_t *>(p);
 }
 
+// Reductions over each row of 16 lanes with DPP lane permutes (no LDS): swap
+// neighbours, swap pairs, mirror within 8 lanes, mirror within 16 lanes. Every
+// lane of the row ends with the row's result.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  return fmaxf(v, dpp<kDppMirror>(v));
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  return v + dpp<kDppMirror>(v);
+}
+
+// 2^x on the hardware exp unit (inputs here are <= 0; -inf gives 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

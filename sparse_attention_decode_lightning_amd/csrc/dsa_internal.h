@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/dsa.h"
+#include "dsa.h"
 
 namespace dsa {
 
@@ -36,10 +36,12 @@ hipError_t launch_indexer_scores(const BatchArgs &bt, const void *q_idx, int32_t
                                  hipStream_t stream);
 
 size_t topk_workspace_bytes(int32_t total_q, int32_t max_seq_len, int32_t k);
+bool topk_supported(int32_t max_seq_len, int32_t k);
 hipError_t launch_topk(const BatchArgs &bt, const float *scores, int64_t ld_scores, int32_t k,
                        int32_t *indices, void *workspace, size_t ws_bytes, hipStream_t stream);
 
 int mla_num_splits(int32_t total_q, int32_t n_heads, int32_t d_latent, int32_t k);
+int mla_max_k();  // largest k of the 64-head bf16 MFMA path
 size_t mla_workspace_bytes(int32_t total_q, int32_t n_heads, int32_t d_latent, int32_t k);
 hipError_t launch_sparse_mla(const BatchArgs &bt, const void *q, int32_t q_dtype, int32_t n_heads,
                              int32_t d_latent, int32_t d_rope, const CacheArgs &kv,

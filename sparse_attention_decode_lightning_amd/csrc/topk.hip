@@ -2,18 +2,27 @@
 // Request-to-Backend Inference Path", section "8. The SFA backend, step by
 // step": the indexer returns token positions, 2,048 per query).
 //
-// One 1024-thread workgroup selects one row by radix select:
-//  * scores map to order-preserving 32-bit keys (-0.0 first folded into +0.0,
-//    so the two compare equal);
-//  * four 8-bit digit passes, most significant first, each a histogram of the
-//    keys that still match the chosen prefix (one private histogram per wave to
-//    spread LDS atomics), find the k-th largest key tau and how many keys equal
-//    to tau must be taken;
-//  * one ordered pass then keeps every key > tau and the first `need` keys
-//    == tau in position order; wave ballots give each kept position its rank,
-//    so the output is written in ascending position order without a sort.
-// Rows of up to kCacheKeys candidates are staged once in LDS as keys; longer
-// rows are re-read from global memory (L2) on every pass.
+// Order: larger score first; equal scores by lower position first; -0.0 is
+// folded into +0.0 so the two compare equal. Scores map to order-preserving
+// 32-bit keys, so the order is (key descending, position ascending).
+//
+// One 1024-thread workgroup selects among at most kChunk candidates held in
+// LDS as keys:
+//  * three radix passes (11, 11 and 10 bits, most significant first) over the
+//    candidates that still match the chosen prefix find the k-th largest key
+//    tau and how many keys equal to tau must be kept ("need"); each pass is a
+//    shared LDS histogram followed by a suffix scan (wave shuffles plus one
+//    exchange of wave totals);
+//  * one ordered pass: each thread owns a contiguous run of candidates, counts
+//    its keys > tau and == tau, and a block-wide exclusive scan of those counts
+//    gives every kept candidate its output slot, so positions come out in
+//    ascending order with no sort.
+// Rows longer than kChunk run in two phases: phase 1 selects the top-k of each
+// kChunk-position chunk (one workgroup per row and chunk), phase 2 selects the
+// top-k among the chunks' survivors (one workgroup per row). This is exact: a
+// position in the row's top-k is also in its chunk's top-k under the same
+// order, and the survivors stay in ascending position order when the chunks'
+// lists are concatenated.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -22,7 +31,8 @@ namespace {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kCacheKeys = 32768;
+constexpr int kChunk = 32768;  // candidates per workgroup (keys cached in LDS)
+constexpr int kBins = 2048;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -30,130 +40,249 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <bool CACHED>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
-    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
-    int total_q, int max_seq_len, const float *__restrict__ scores, int64_t ld, int k,
-    int32_t *__restrict__ indices) {
-  extern __shared__ uint32_t cache[];
-  __shared__ uint32_t hist[kTopkWaves][256];
-  __shared__ uint32_t suffix[256];
-  __shared__ uint32_t wave_eq[kTopkWaves], wave_sel[kTopkWaves];
-  __shared__ uint32_t s_digit, s_need;
+struct TopkShared {
+  uint32_t hist[kBins];
+  uint32_t wave_tot[kTopkWaves];
+  uint32_t digit, need;
+};
 
-  const int row = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row).t + 1;
-  int32_t *out = indices + (int64_t)row * k;
-  if (n <= k) {
-    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
-    return;
+// Inclusive prefix sum over the 1024 threads of the block (v per thread).
+__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, TopkShared &sh) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t u = __shfl_up(v, off);
+    if (lane >= off) v += u;
   }
-  const float *src = scores + (int64_t)row * ld;
-  if constexpr (CACHED) {
-    for (int i = tid; i < n; i += kTopkThreads) cache[i] = order_key(src[i]);
-  }
-  auto key_at = [&](int i) -> uint32_t {
-    if constexpr (CACHED) return cache[i];
-    else return order_key(src[i]);
-  };
+  if (lane == 63) sh.wave_tot[wv] = v;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) before += w < wv ? sh.wave_tot[w] : 0u;
+  __syncthreads();
+  return v + before;
+}
 
-  uint32_t prefix = 0, mask = 0;
-  uint32_t need = (uint32_t)k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    uint32_t *hflat = &hist[0][0];
-    for (int i = tid; i < kTopkWaves * 256; i += kTopkThreads) hflat[i] = 0;
+// Finds tau (the k-th largest key among keys[0..n)) and how many keys equal to
+// tau belong to the top-k. Requires n > k.
+__device__ void radix_select(const uint32_t *keys, int n, uint32_t k, TopkShared &sh,
+                             uint32_t &tau, uint32_t &need_out) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0, need = k;
+  const int shifts[3] = {21, 10, 0};
+  const uint32_t widths[3] = {11, 11, 10};
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = shifts[pass];
+    const uint32_t dmask = (1u << widths[pass]) - 1u;
+    for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += kTopkThreads) {
-      const uint32_t key = key_at(i);
-      if ((key & mask) == prefix) atomicAdd(&hist[wv][(key >> shift) & 255u], 1u);
+      const uint32_t key = keys[i];
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
-    if (tid < 256) {
-      uint32_t c = 0;
-#pragma unroll
-      for (int w = 0; w < kTopkWaves; ++w) c += hist[w][tid];
-      suffix[tid] = c;
+    // thread t owns digits 2047-2t and 2046-2t, so a prefix over threads is a
+    // suffix over digits
+    const int d_hi = kBins - 1 - 2 * tid, d_lo = d_hi - 1;
+    const uint32_t h_hi = sh.hist[d_hi], h_lo = sh.hist[d_lo];
+    const uint32_t incl = block_inclusive_scan(h_hi + h_lo, sh);
+    const uint32_t s_lo = incl;           // candidates with digit >= d_lo
+    const uint32_t s_hi = incl - h_lo;    // candidates with digit >= d_hi
+    if (s_hi >= need && s_hi - h_hi < need) {
+      sh.digit = (uint32_t)d_hi;
+      sh.need = need - (s_hi - h_hi);
+    } else if (s_lo >= need && s_lo - h_lo < need) {
+      sh.digit = (uint32_t)d_lo;
+      sh.need = need - (s_lo - h_lo);
     }
     __syncthreads();
-    // inclusive suffix sums: suffix[d] = number of candidates with digit >= d
-    for (int off = 1; off < 256; off <<= 1) {
-      uint32_t v = 0;
-      if (tid < 256 && tid + off < 256) v = suffix[tid + off];
-      __syncthreads();
-      if (tid < 256) suffix[tid] += v;
-      __syncthreads();
-    }
-    if (tid < 256) {
-      const uint32_t above = tid == 255 ? 0u : suffix[tid + 1];
-      if (suffix[tid] >= need && above < need) {
-        s_digit = (uint32_t)tid;
-        s_need = need - above;
-      }
-    }
-    __syncthreads();
-    prefix |= s_digit << shift;
-    mask |= 255u << shift;
-    need = s_need;
+    prefix |= sh.digit << shift;
+    mask |= dmask << shift;
+    need = sh.need;
     __syncthreads();
   }
+  tau = prefix;
+  need_out = need;
+}
 
-  // Ordered selection: keys > tau, then the first `need` keys == tau.
-  const uint32_t tau = prefix;
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
-  uint32_t base_eq = 0, base_sel = 0;
-  for (int c0 = 0; c0 < n; c0 += kTopkThreads) {
-    const int i = c0 + tid;
-    const uint32_t key = i < n ? key_at(i) : 0u;
-    const bool gt = i < n && key > tau;
-    const bool eq = i < n && key == tau;
-    const uint64_t beq = __ballot(eq);
-    if (lane == 0) wave_eq[wv] = (uint32_t)__popcll(beq);
-    __syncthreads();
-    uint32_t eq_rank = base_eq + (uint32_t)__popcll(beq & lt_mask), eq_tot = 0;
-#pragma unroll
-    for (int w = 0; w < kTopkWaves; ++w) {
-      const uint32_t v = wave_eq[w];
-      eq_rank += w < wv ? v : 0u;
-      eq_tot += v;
-    }
-    const bool sel = gt || (eq && eq_rank < need);
-    const uint64_t bsel = __ballot(sel);
-    if (lane == 0) wave_sel[wv] = (uint32_t)__popcll(bsel);
-    __syncthreads();
-    uint32_t slot = base_sel + (uint32_t)__popcll(bsel & lt_mask), sel_tot = 0;
-#pragma unroll
-    for (int w = 0; w < kTopkWaves; ++w) {
-      const uint32_t v = wave_sel[w];
-      slot += w < wv ? v : 0u;
-      sel_tot += v;
-    }
-    if (sel && slot < (uint32_t)k) out[slot] = i;
-    base_eq += eq_tot;
-    base_sel += sel_tot;
-    __syncthreads();
+// Writes the kept candidates' positions in candidate order: every key > tau
+// and the first `need` keys == tau. pos_of(i) gives candidate i's position;
+// out_key (optional) also receives the kept keys.
+template <typename PosFn>
+__device__ void ordered_emit(const uint32_t *keys, int n, uint32_t tau, uint32_t need,
+                             TopkShared &sh, PosFn pos_of, int32_t *out_pos,
+                             uint32_t *out_key) {
+  const int tid = threadIdx.x;
+  const int per = (n + kTopkThreads - 1) / kTopkThreads;
+  const int b0 = min(n, tid * per), b1 = min(n, b0 + per);
+  uint32_t gt = 0, eq = 0;
+  for (int i = b0; i < b1; ++i) {
+    const uint32_t key = keys[i];
+    gt += key > tau;
+    eq += key == tau;
   }
+  // counts fit in 16 bits (n <= kChunk), so one scan carries both
+  const uint32_t packed = block_inclusive_scan((gt << 16) | eq, sh) - ((gt << 16) | eq);
+  uint32_t gt_before = packed >> 16, eq_before = packed & 0xFFFFu;
+  for (int i = b0; i < b1; ++i) {
+    const uint32_t key = keys[i];
+    if (key > tau) {
+      const uint32_t slot = gt_before + min(eq_before, need);
+      out_pos[slot] = pos_of(i);
+      if (out_key) out_key[slot] = key;
+      ++gt_before;
+    } else if (key == tau) {
+      if (eq_before < need) {
+        const uint32_t slot = gt_before + eq_before;
+        out_pos[slot] = pos_of(i);
+        if (out_key) out_key[slot] = key;
+      }
+      ++eq_before;
+    }
+  }
+}
+
+// Single-phase row top-k (rows of at most kChunk candidates), or phase 1 of
+// the two-phase path (one chunk of a long row; survivors to the workspace).
+template <bool PHASE1>
+__global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
+    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
+    int total_q, int max_seq_len, const float *__restrict__ scores, int64_t ld, int k,
+    int32_t *__restrict__ indices, int n_chunks, uint32_t *__restrict__ ws_key,
+    int32_t *__restrict__ ws_pos) {
+  extern __shared__ uint32_t s_keys[];
+  __shared__ TopkShared sh;
+  const int row = PHASE1 ? blockIdx.x / n_chunks : blockIdx.x;
+  const int chunk = PHASE1 ? blockIdx.x % n_chunks : 0;
+  const int tid = threadIdx.x;
+  const int n_row = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row).t + 1;
+  if (!PHASE1 && n_row <= k) {
+    int32_t *out = indices + (int64_t)row * k;
+    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n_row ? i : -1;
+    return;
+  }
+  const int c0 = chunk * kChunk;
+  const int n = min(kChunk, n_row - c0);
+  if (n <= 0) return;
+  const float *src = scores + (int64_t)row * ld + c0;
+  for (int i = tid; i < n; i += kTopkThreads) s_keys[i] = order_key(src[i]);
+  __syncthreads();
+  int32_t *out_pos;
+  uint32_t *out_key = nullptr;
+  if constexpr (PHASE1) {
+    const int64_t base = ((int64_t)row * n_chunks + chunk) * k;
+    out_pos = ws_pos + base;
+    out_key = ws_key + base;
+    if (n <= k) {  // the whole chunk survives
+      for (int i = tid; i < n; i += kTopkThreads) {
+        out_pos[i] = c0 + i;
+        out_key[i] = s_keys[i];
+      }
+      return;
+    }
+  } else {
+    out_pos = indices + (int64_t)row * k;
+  }
+  uint32_t tau, need;
+  radix_select(s_keys, n, (uint32_t)k, sh, tau, need);
+  ordered_emit(s_keys, n, tau, need, sh, [&](int i) { return c0 + i; }, out_pos, out_key);
+}
+
+// Phase 2: top-k among the concatenated chunk survivors of one row.
+__global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
+    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
+    int total_q, int max_seq_len, int k, int n_chunks, const uint32_t *__restrict__ ws_key,
+    const int32_t *__restrict__ ws_pos, int32_t *__restrict__ indices) {
+  extern __shared__ uint32_t s_keys[];
+  __shared__ TopkShared sh;
+  __shared__ int s_start[64];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n_row = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row).t + 1;
+  int32_t *out = indices + (int64_t)row * k;
+  if (n_row <= k) {
+    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n_row ? i : -1;
+    return;
+  }
+  // survivors of chunk c: min(k, its length), stored at [c * k, ...)
+  if (tid == 0) {
+    int acc = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      s_start[c] = acc;
+      const int len = max(0, min(kChunk, n_row - c * kChunk));
+      acc += min(k, len);
+    }
+    s_start[n_chunks] = acc;
+  }
+  __syncthreads();
+  const int n = s_start[n_chunks];
+  const int64_t base = (int64_t)row * n_chunks * k;
+  for (int c = 0; c < n_chunks; ++c) {
+    const int m = s_start[c + 1] - s_start[c];
+    for (int i = tid; i < m; i += kTopkThreads)
+      s_keys[s_start[c] + i] = ws_key[base + (int64_t)c * k + i];
+  }
+  __syncthreads();
+  auto pos_of = [&](int i) -> int32_t {
+    int c = 0;
+    while (c + 1 < n_chunks && s_start[c + 1] <= i) ++c;
+    return ws_pos[base + (int64_t)c * k + (i - s_start[c])];
+  };
+  if (n <= k) {  // a single chunk already reduced to exactly k survivors
+    for (int i = tid; i < n; i += kTopkThreads) out[i] = pos_of(i);
+    return;
+  }
+  uint32_t tau, need;
+  radix_select(s_keys, n, (uint32_t)k, sh, tau, need);
+  ordered_emit(s_keys, n, tau, need, sh, pos_of, out, nullptr);
+}
+
+int chunks_of(int32_t max_seq_len) { return (max_seq_len + kChunk - 1) / kChunk; }
+
+bool two_phase(int32_t max_seq_len) { return max_seq_len > kChunk; }
+
+hipError_t set_lds(const void *fn, size_t bytes) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 }  // namespace
 
-size_t topk_workspace_bytes(int32_t, int32_t, int32_t) { return 0; }
+size_t topk_workspace_bytes(int32_t total_q, int32_t max_seq_len, int32_t k) {
+  if (!two_phase(max_seq_len) || total_q < 1 || k < 1) return 0;
+  return (size_t)total_q * chunks_of(max_seq_len) * k * (sizeof(uint32_t) + sizeof(int32_t));
+}
+
+bool topk_supported(int32_t max_seq_len, int32_t k) {
+  if (!two_phase(max_seq_len)) return true;
+  const int nc = chunks_of(max_seq_len);
+  return nc < 64 && (int64_t)nc * (k < kChunk ? k : kChunk) <= kChunk;
+}
 
 hipError_t launch_topk(const BatchArgs &bt, const float *scores, int64_t ld, int32_t k,
-                       int32_t *indices, void *, size_t, hipStream_t stream) {
+                       int32_t *indices, void *workspace, size_t, hipStream_t stream) {
   if (bt.total_q == 0) return hipSuccess;
-  if (bt.max_seq_len <= kCacheKeys) {
-    const size_t lds = (size_t)(bt.max_seq_len > 0 ? bt.max_seq_len : 1) * sizeof(uint32_t);
-    hipError_t e = hipFuncSetAttribute((const void *)topk_kernel<true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_kernel<true>, dim3(bt.total_q), dim3(kTopkThreads), lds, stream,
-                       bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, scores, ld, k, indices);
-  } else {
-    hipLaunchKernelGGL(topk_kernel<false>, dim3(bt.total_q), dim3(kTopkThreads), 0, stream,
-                       bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, scores, ld, k, indices);
+  const size_t lds = (size_t)kChunk * sizeof(uint32_t);
+  hipError_t e;
+  if (!two_phase(bt.max_seq_len)) {
+    if ((e = set_lds((const void *)topk_rows_kernel<false>, lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_rows_kernel<false>, dim3(bt.total_q), dim3(kTopkThreads), lds, stream,
+                       bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, scores, ld, k,
+                       indices, 1, nullptr, nullptr);
+    return hipGetLastError();
   }
+  const int nc = chunks_of(bt.max_seq_len);
+  uint32_t *ws_key = static_cast<uint32_t *>(workspace);
+  int32_t *ws_pos = reinterpret_cast<int32_t *>(ws_key + (size_t)bt.total_q * nc * k);
+  if ((e = set_lds((const void *)topk_rows_kernel<true>, lds)) != hipSuccess) return e;
+  if ((e = set_lds((const void *)topk_merge_kernel, lds)) != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_rows_kernel<true>, dim3(bt.total_q * nc), dim3(kTopkThreads), lds,
+                     stream, bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, scores,
+                     ld, k, indices, nc, ws_key, ws_pos);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(bt.total_q), dim3(kTopkThreads), lds, stream,
+                     bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, k, nc, ws_key,
+                     ws_pos, indices);
   return hipGetLastError();
 }
 

@@ -94,14 +94,17 @@ def test_indexer_rejects_bad_arguments(kw, code):
     assert _idx(**kw) == code
 
 
-def _topk(b=None, s=FAKE, ld=256, k=64, idx=FAKE):
+def _topk(b=None, s=FAKE, ld=256, k=64, idx=FAKE, ws=None, wsb=0):
     b = _batch() if b is None else b
-    return L.lib.dsa_topk(ctypes.byref(b) if b is not False else None, s, ld, k, idx, None, 0, None)
+    return L.lib.dsa_topk(ctypes.byref(b) if b is not False else None, s, ld, k, idx, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(b=False), 1), (dict(s=None), 1), (dict(idx=None), 1),
     (dict(k=0), 2), (dict(ld=100), 2), (dict(idx=FAKE + 2), 2), (dict(b=_batch(total_q=-1)), 2),
+    (dict(b=_batch(max_seq_len=100000, bt_stride=2000), ld=100000, k=2048), 4),
+    (dict(b=_batch(max_seq_len=100000, bt_stride=2000), ld=100000, k=2048, ws=FAKE, wsb=16), 4),
+    (dict(b=_batch(max_seq_len=1 << 21, bt_stride=1 << 16), ld=1 << 21, k=2048), 5),
 ])
 def test_topk_rejects_bad_arguments(kw, code):
     assert _topk(**kw) == code
@@ -131,6 +134,7 @@ def test_mla_rejects_bad_arguments(kw, code):
 
 def test_workspace_sizes_are_pure_functions_of_bounds():
     assert L.lib.dsa_topk_workspace_size(32, 8192, 2048) == 0
+    assert L.lib.dsa_topk_workspace_size(32, 245760, 2048) == 32 * 8 * 2048 * 8
     s = L.lib.dsa_sparse_mla_workspace_size(32, 64, 512, 2048)
     assert s > 0 and s == L.lib.dsa_sparse_mla_workspace_size(32, 64, 512, 2048)
     assert L.lib.dsa_sparse_mla_workspace_size(4096, 64, 512, 2048) == 0

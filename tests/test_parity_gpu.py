@@ -32,6 +32,8 @@ SMALL_CASES = {
     "idx64_heads": small_variant(BF16_DECODE, batch=2, lens=(500, 260), idx_heads=64, topk=128),
     "idx16_heads_multiq": small_variant("verify_b8_l240k", batch=2, lens=(400, 90), q_per_seq=5,
                                         idx_heads=16, topk=64),
+    "topk_two_phase": small_variant("indexshare_b64", batch=4, lens=(70000, 33000, 5000, 300),
+                                    topk=512, n_layers=1),
     "mla_generic_bf16": small_variant(BF16_DECODE, batch=2, lens=(300, 129), mla_heads=16,
                                       d_latent=128, d_rope=32, topk=100),
 }
@@ -131,3 +133,48 @@ def test_full_size_sampled_parity(name, dev):
     for l, (out, lse) in enumerate(outs):
         assert torch.isfinite(out).all()
         P.check_mla(inp, l, idx, out, lse, rows, host)
+
+
+def test_graph_replay_matches_eager(dev):
+    """The three calls captured into a HIP graph replay bit-exactly, replay after replay,
+    with unrelated eager work and synchronizations in between."""
+    import sparse_attention_decode_lightning_amd as dsa
+
+    wl = small_variant("indexshare_b64", batch=3, lens=(3000, 2100, 40000), topk=512, n_layers=2)
+    inp = to_device(make_inputs(wl), dev)
+    b, keys = P.batch_of(inp), P.keys_of(inp)
+    T = inp.total_q
+    scores = torch.zeros((T, inp.max_seq_len), dtype=torch.float32, device=dev)
+    idx = torch.zeros((T, wl.topk), dtype=torch.int32, device=dev)
+    outs = [torch.zeros((T, wl.mla_heads, wl.d_latent), dtype=torch.float32, device=dev)
+            for _ in range(wl.n_layers)]
+    tk_ws = torch.zeros(max(16, dsa.topk_workspace_size(T, inp.max_seq_len, wl.topk)),
+                        dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(16, dsa.sparse_mla_workspace_size(T, wl.mla_heads, wl.d_latent, wl.topk)),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        dsa.indexer_scores(b, inp.q_idx, inp.w, keys, scores=scores)
+        dsa.topk(b, scores, wl.topk, indices=idx, workspace=tk_ws)
+        for l in range(wl.n_layers):
+            dsa.sparse_mla_fwd(b, inp.q_mla[l], dsa.PagedCache(inp.kv_cache[l]), idx, wl.d_latent,
+                               wl.scale, out=outs[l], workspace=ws, want_lse=False)
+
+    step()
+    torch.cuda.synchronize()
+    ref_idx, ref_out = idx.clone(), [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        idx.fill_(-7)
+        for o in outs:
+            o.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=dev).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_idx), f"replay {i}: indices differ"
+        for o, r in zip(outs, ref_out):
+            assert torch.equal(o, r), f"replay {i}: outputs differ"
+        del junk
