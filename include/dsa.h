@@ -11,8 +11,8 @@
  *          I[t, s] = sum_j w[t, j] * ReLU(q_idx[t, j, :] . k_idx[s, :]),  s <= t
  *   2. dsa_topk — the k best token positions per query row ("GLM-5.2 on vLLM
  *      Ascend: Request-to-Backend Inference Path", section "8. The SFA
- *      backend, step by step": the operator asks for 2,048 positions and the
- *      indexer selects tokens, not blocks);
+ *      backend, step by step": 2,048 positions are requested, and what is
+ *      selected is individual token positions, not compressed blocks);
  *   3. dsa_sparse_mla_fwd — absorbed MLA attention over only the selected
  *      cache rows ("vLLM Inference Path: GLM-5.2 as an Example", sections
  *      "MLA Projections and KV State" and "Sparse MLA Attention"; "Making

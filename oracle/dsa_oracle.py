@@ -15,12 +15,13 @@ the pages describe the method:
   plus a 64-d RoPE key per token; (section "Sparse MLA Attention"): attention
   reads only the selected positions and the causal mask still applies.
 * "Making GLM-5.2 Sparse on TPUs" (section "Separate the indexer from the
-  attention it controls"): the score is a weighted sum of ReLU-transformed
-  query-key dot products; absorbed MLA moves the key projection onto the query
-  and applies the value projection after the weighted sum of latents; the
-  attention scale stays tied to 192 + 64, not 576. (Section "Pack requests and
-  reuse prefixes"): a query at local offset i after a prefix of length P sits
-  at absolute position P + i.
+  attention it controls"): each head's query-key dot product goes through a
+  ReLU before the heads are combined with per-head weights; in the absorbed
+  form the query carries the key projection and the latents themselves are
+  the values (the value projection comes after the attention sum); the scale
+  comes from the 192 + 64 query/key width rather than from 576. (Section
+  "Pack requests and reuse prefixes"): a query at local offset i after a
+  prefix of length P sits at absolute position P + i.
 * "GLM-5.2 on vLLM Ascend: Request-to-Backend Inference Path" (section "8. The
   SFA backend, step by step"): the new token's keys are written to the paged
   cache before selection, indices are token positions, and the indexer's keys

@@ -25,26 +25,19 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
-// OCP E4M3FN byte -> bf16 bits, exact (every e4m3fn value is a bf16 value).
-// Normal codes (exponent field e >= 1): 2^(e-7) * (1 + m/8) -> bf16 exponent
-// e + 120 with the three mantissa bits on top; subnormals m * 2^-9 go through
-// an exact int -> float conversion; S.1111.111 is NaN.
-__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t byte) {
-  uint32_t sign = (byte & 0x80u) << 8;
-  uint32_t em = byte & 0x7Fu;
-  uint32_t normal = (em << 4) + (120u << 7);
-  uint32_t sub = __float_as_uint((float)em * 0.001953125f) >> 16;
-  uint32_t mag = em >= 8u ? normal : sub;
-  mag = em == 0x7Fu ? 0x7FC0u : mag;
-  return sign | mag;
-}
-
-// Four e4m3 bytes packed in a dword -> two dwords of bf16 pairs (low byte first).
+// OCP E4M3FN -> bf16 on the gfx950 conversion unit (scale 1.0, so exact:
+// every e4m3fn value is a bf16 value). Four bytes of a dword -> two dwords of
+// bf16 pairs, lowest byte first.
 __device__ __forceinline__ u32x2_t e4m3x4_to_bf16x4(uint32_t w) {
   u32x2_t r;
-  r.x = e4m3_to_bf16(w & 0xFFu) | (e4m3_to_bf16((w >> 8) & 0xFFu) << 16);
-  r.y = e4m3_to_bf16((w >> 16) & 0xFFu) | (e4m3_to_bf16(w >> 24) << 16);
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
   return r;
+}
+
+// One OCP E4M3FN byte -> fp32 (exact).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
 }
 
 __device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {

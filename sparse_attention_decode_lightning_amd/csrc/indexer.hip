@@ -12,7 +12,7 @@
 // key, so ReLU, the per-head weight and the in-lane part of the head sum run
 // in registers, and two cross-lane adds finish the head sum. e4m3 keys are
 // widened exactly to bf16 in registers; their per-token scale multiplies each
-// head's dot product before the ReLU, exactly as k = scale * e4m3 defines.
+// head's dot product before the ReLU, so k = scale * e4m3 holds for any scale.
 // Keys are read straight from HBM into MFMA operand registers, every key byte
 // once per query group; each lane's 16-byte loads from one key row keep all
 // of a 64-byte (bf16) or 32-byte (fp8) run in one instruction.
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void indexer_generic_kernel(
       if constexpr (KDT == DSA_F32) kv = reinterpret_cast<const float *>(kdata)[kr * D + d];
       else if constexpr (KDT == DSA_BF16)
         kv = bf16_to_f32(reinterpret_cast<const uint16_t *>(kdata)[kr * D + d]);
-      else kv = bf16_to_f32(e4m3_to_bf16(reinterpret_cast<const uint8_t *>(kdata)[kr * D + d]));
+      else kv = e4m3_to_f32(reinterpret_cast<const uint8_t *>(kdata)[kr * D + d]);
       float qv;
       if constexpr (sizeof(QT) == 4) qv = qp[d];
       else qv = bf16_to_f32(qp[d]);

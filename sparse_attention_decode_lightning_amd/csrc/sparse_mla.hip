@@ -58,6 +58,7 @@ constexpr int kMinRowsPerSplit = 128;
 constexpr int kXcds = 8;
 constexpr int kMaxRowsPerSplit = 2048;
 constexpr int kMaxSplits = 64;
+constexpr int kRowBufs = 3;  // row tiles in LDS: computed, next, landing
 constexpr float kLazy = 8.0f;  // log2 headroom before the reference maximum moves
 
 // Row <-> MFMA k-slot map of the PV contraction. Lane group g of the value
@@ -93,13 +94,13 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_bf16_kernel(
     int page_size, const int32_t *__restrict__ indices, int k, int n_splits, int rows_per_split,
     float scale_log2, float *__restrict__ out, float *__restrict__ lse,
     float *__restrict__ ws_acc, float *__restrict__ ws_ml) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_rows[2][kTileN * kRowStride];
+  __shared__ __attribute__((aligned(16))) uint8_t s_rows[kRowBufs][kTileN * kRowStride];
   __shared__ __attribute__((aligned(16))) uint8_t s_phi[kH * kPStride];
   __shared__ __attribute__((aligned(16))) uint8_t s_plo[kH * kPStride];
   __shared__ f32x4_t s_xchg[8][2][kWave];  // partial logits handed to the other dim half
   __shared__ float s_alpha[kH];
-  __shared__ float s_ml[kH][2];
-  __shared__ int s_rescale[2];  // some head's reference max moved in tile parity 0 / 1
+  __shared__ float s_ml[kH][2][2];  // per head, per dim half: (m, l)
+  __shared__ int s_rescale[2];      // some head's reference max moved (tile parity)
   __shared__ __attribute__((aligned(16))) int32_t s_rowid[kMaxRowsPerSplit + kTileN];
 
   // XCD-aware numbering: block id = ((row / 8) * n_splits + split) * 8 + row % 8
@@ -120,9 +121,15 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_bf16_kernel(
   const int nrows = max(0, slot_end - slot_begin);
   const int ntiles = (nrows + kTileN - 1) / kTileN;
   const int32_t *idx_row = indices + (int64_t)row * k;
+  auto rowid_of = [&](int i) -> int32_t {  // physical row of slot i of the split, or -1
+    if (i >= nrows) return -1;
+    const int pos = idx_row[slot_begin + i];
+    if (pos < 0 || pos > t) return -1;
+    return (int32_t)paged_row(block_table, bt_stride, b, pos, page_size, num_pages);
+  };
 
   // Query block of heads 16hg.. over dim half kh: lane (g, i) holds head
-  // 16hg + i, dims 288kh + 32s + 8g .. +8. Issued before anything waits.
+  // 16hg + i, dims 288kh + 32s + 8g .. +8.
   u32x4_t qf[kHalfSteps];
   {
     const uint16_t *qp = q + ((int64_t)row * kH + 16 * hg + j) * kD + 288 * kh + 8 * g;
@@ -130,50 +137,25 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_bf16_kernel(
     for (int s = 0; s < kHalfSteps; ++s) qf[s] = ldg16(qp + 32 * s);
   }
 
-  // Translate every selected position of the split once (padding to whole
-  // tiles with -1), so the tile loop never waits on index or block-table reads.
-  for (int i = tid; i < ntiles * kTileN; i += kMlaThreads) {
-    int32_t rid = -1;
-    if (i < nrows) {
-      const int pos = idx_row[slot_begin + i];
-      if (pos >= 0 && pos <= t)
-        rid = (int32_t)paged_row(block_table, bt_stride, b, pos, page_size, num_pages);
-    }
-    s_rowid[i] = rid;
-  }
-
-  f32x4_t o[4][4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) o[mt][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  // m_run is each head's reference maximum: probabilities are 2^(x - m_run),
-  // and m_run only moves (with a rescale of everything accumulated so far)
-  // when a logit exceeds it by more than kLazy, so p <= 2^kLazy.
-  float m_run[4], l_run[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m_run[r] = -INFINITY;
-    l_run[r] = 0.0f;
-  }
-
   // Gather map of a 32-row tile (72 chunks of 16 bytes per row): wave wv owns
   // rows 4wv..4wv+3; chunks 0..63 of row 4wv+m go to lane = chunk, chunks
   // 64..71 of row 4wv + lane/8 to lanes 0..31.
   u32x4_t buf[5];
-  auto issue_loads = [&](int tile) {
-    const int4 rid4 = *reinterpret_cast<const int4 *>(&s_rowid[tile * kTileN + 4 * wv]);
-    const int rids[4] = {__builtin_amdgcn_readfirstlane(rid4.x),
-                         __builtin_amdgcn_readfirstlane(rid4.y),
-                         __builtin_amdgcn_readfirstlane(rid4.z),
-                         __builtin_amdgcn_readfirstlane(rid4.w)};
+  auto load_rows = [&](int r0, int r1, int r2, int r3) {
+    const int rids[4] = {r0, r1, r2, r3};
 #pragma unroll
     for (int m = 0; m < 4; ++m)
       buf[m] = rids[m] >= 0 ? ldg16(kv + (int64_t)rids[m] * kRowBytes + 16 * lane)
                             : u32x4_t{0u, 0u, 0u, 0u};
-    const int r5 = s_rowid[tile * kTileN + 4 * wv + (lane >> 3)];
+    const int q4 = lane >> 3;
+    const int r5 = q4 == 0 ? r0 : (q4 == 1 ? r1 : (q4 == 2 ? r2 : r3));
     buf[4] = (lane < 32 && r5 >= 0) ? ldg16(kv + (int64_t)r5 * kRowBytes + 16 * (64 + (lane & 7)))
                                     : u32x4_t{0u, 0u, 0u, 0u};
+  };
+  auto issue_loads = [&](int tile) {
+    const int4 rid4 = *reinterpret_cast<const int4 *>(&s_rowid[tile * kTileN + 4 * wv]);
+    load_rows(__builtin_amdgcn_readfirstlane(rid4.x), __builtin_amdgcn_readfirstlane(rid4.y),
+              __builtin_amdgcn_readfirstlane(rid4.z), __builtin_amdgcn_readfirstlane(rid4.w));
   };
   auto store_tile = [&](int tb) {
     uint8_t *base = s_rows[tb] + (4 * wv) * kRowStride;
@@ -184,51 +166,79 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_bf16_kernel(
       *reinterpret_cast<u32x4_t *>(base + (lane >> 3) * kRowStride + 16 * (64 + (lane & 7))) =
           buf[4];
   };
+  // partial logits of heads 16hg + 4g + r against rows 16nt + j of a tile,
+  // dims of half kh, with operand reads one k-step ahead of the MFMAs
+  auto logits = [&](int tb, f32x4_t (&acc)[2]) {
+    const uint8_t *rp = s_rows[tb] + j * kRowStride + 576 * kh + 16 * g;
+    u32x4_t bcur[2], bnext[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      bcur[nt] = *reinterpret_cast<const u32x4_t *>(rp + nt * 16 * kRowStride);
+    }
+#pragma unroll
+    for (int s = 0; s < kHalfSteps; ++s) {
+      if (s + 1 < kHalfSteps) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          bnext[nt] = *reinterpret_cast<const u32x4_t *>(rp + nt * 16 * kRowStride + 64 * (s + 1));
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma_16x16x32_bf16(qf[s], bcur[nt], acc[nt]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) bcur[nt] = bnext[nt];
+    }
+  };
 
-  if (tid < 2) s_rescale[tid] = 0;
-  __syncthreads();
+  // ---- prologue: tile 0 is gathered before the full row table exists ----
   if (ntiles > 0) {
-    issue_loads(0);
-    store_tile(0);
-    if (ntiles > 1) issue_loads(1);
+    const int mine = lane < 4 ? rowid_of(4 * wv + lane) : -1;
+    load_rows(__builtin_amdgcn_readlane(mine, 0), __builtin_amdgcn_readlane(mine, 1),
+              __builtin_amdgcn_readlane(mine, 2), __builtin_amdgcn_readlane(mine, 3));
   }
-  __syncthreads();
+  // translate every selected position of the split once (padding to whole
+  // tiles with -1), so the tile loop never waits on index or block-table reads
+  for (int i = tid; i < ntiles * kTileN; i += kMlaThreads) s_rowid[i] = rowid_of(i);
+  if (tid < 2) s_rescale[tid] = 0;
 
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const uint8_t *rows = s_rows[tile & 1];
-    // 1. partial logits of heads 16hg + 4g + r against rows 16nt + j, dims of half kh
-    f32x4_t sacc[2];
-    {
-      const uint8_t *rp = rows + j * kRowStride + 576 * kh + 16 * g;
-      u32x4_t bcur[2], bnext[2];
+  f32x4_t o[4][4];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        sacc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        bcur[nt] = *reinterpret_cast<const u32x4_t *>(rp + nt * 16 * kRowStride);
-      }
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int s = 0; s < kHalfSteps; ++s) {
-        if (s + 1 < kHalfSteps) {
+    for (int nt = 0; nt < 4; ++nt) o[mt][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // m_run is each head's reference maximum: probabilities are 2^(x - m_run),
+  // and m_run only moves (with a rescale of everything accumulated so far)
+  // when a logit exceeds it by more than kLazy, so p <= 2^kLazy. l_run sums
+  // the probabilities of this wave's 16 rows of every tile.
+  float m_run[4], l_run[4];
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            bnext[nt] =
-                *reinterpret_cast<const u32x4_t *>(rp + nt * 16 * kRowStride + 64 * (s + 1));
-        }
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) sacc[nt] = mfma_16x16x32_bf16(qf[s], bcur[nt], sacc[nt]);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) bcur[nt] = bnext[nt];
-      }
+  for (int r = 0; r < 4; ++r) {
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.0f;
+  }
+
+  f32x4_t sacc[2], snext[2];
+  if (ntiles > 0) {
+    store_tile(0);
+    __syncthreads();  // row table and tile 0 visible
+    if (ntiles > 1) issue_loads(1);
+    logits(0, sacc);
+    if (ntiles > 1) {
+      store_tile(1);
+      if (ntiles > 2) issue_loads(2);
     }
     s_xchg[wv][0][lane] = sacc[0];
     s_xchg[wv][1][lane] = sacc[1];
-    __syncthreads();  // (A) partial logits exchanged; everyone is past PV(tile - 1)
+  }
+  __syncthreads();  // A(0): partials of tile 0 and tile 1's rows visible
 
-    // 2. the tile after next can now land in the buffer PV(tile - 1) used
-    if (tile + 1 < ntiles) store_tile((tile + 1) & 1);
-    if (tile + 2 < ntiles) issue_loads(tile + 2);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    // a. logits of the next tile start in the matrix pipe while this tile's
+    //    softmax runs on the vector units
+    if (tile + 1 < ntiles) logits((tile + 1) % kRowBufs, snext);
 
-    // 3. full logits and online softmax for this wave's 16 heads over all 32 rows
+    // b. full logits and online softmax of this wave's 16 heads; both waves of
+    //    a head group see all 32 rows (same maximum), wave kh owns rows 16kh + j
     float x[2][4];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -248,13 +258,12 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_bf16_kernel(
       const float m_new = up ? tmax : m_run[r];
       const float m_use = m_new == -INFINITY ? 0.0f : m_new;
       const float alpha = up ? fast_exp2(m_run[r] - m_use) : 1.0f;
-      const float p0 = fast_exp2(x[0][r] - m_use);
-      const float p1 = fast_exp2(x[1][r] - m_use);
-      l_run[r] = l_run[r] * alpha + row16_sum(p0 + p1);
+      const float p = fast_exp2((kh == 0 ? x[0][r] : x[1][r]) - m_use);
+      l_run[r] = l_run[r] * alpha + row16_sum(p);
       m_run[r] = m_new;
       moved |= up;
       if (kh == 0 && j == 0) s_alpha[head] = alpha;
-      pmine[r] = kh == 0 ? p0 : p1;  // wave kh writes rows 16kh + j
+      pmine[r] = p;
     }
     if (kh == 0 && __ballot(moved) != 0 && lane == 0) s_rescale[tile & 1] = 1;
     {
@@ -273,10 +282,16 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_bf16_kernel(
         reinterpret_cast<__bf16 *>(s_plo + (head + 1) * kPStride)[slot] = lo.y;
       }
     }
-    __syncthreads();  // (B) probabilities and rescale factors visible
 
-    // 4. rescale (only when a reference maximum moved) and accumulate P.V
-    //    for dims 64wv .. +64, all heads, K = 32 rows
+    // c. the tile after next lands in the buffer PV(tile - 1) used
+    if (tile + 2 < ntiles) {
+      store_tile((tile + 2) % kRowBufs);
+      if (tile + 3 < ntiles) issue_loads(tile + 3);
+    }
+    __syncthreads();  // B(tile): probabilities and rescale factors visible
+
+    // d. rescale (only when a reference maximum moved) and accumulate P.V for
+    //    dims 64wv .. +64, all heads, K = 32 rows
     if (s_rescale[tile & 1]) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -288,6 +303,7 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_bf16_kernel(
         }
     }
     {
+      const uint8_t *rows = s_rows[tile % kRowBufs];
       // lane (g, i) of transposed load L reads row 16L + 8(g&1) + (g>>1) + 2(i>>2)
       const uint8_t *vbase = rows + (8 * (g & 1) + (g >> 1) + 2 * (j >> 2)) * kRowStride +
                              (64 * wv + 4 * (j & 3)) * 2;
@@ -304,21 +320,30 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_bf16_kernel(
         const u32x4_t pa_hi = *reinterpret_cast<const u32x4_t *>(s_phi + poff);
         const u32x4_t pa_lo = *reinterpret_cast<const u32x4_t *>(s_plo + poff);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          o[mt][nt] = mfma_16x16x32_bf16(pa_hi, vb[nt], o[mt][nt]);
-          o[mt][nt] = mfma_16x16x32_bf16(pa_lo, vb[nt], o[mt][nt]);
-        }
+        for (int nt = 0; nt < 4; ++nt) o[mt][nt] = mfma_16x16x32_bf16(pa_hi, vb[nt], o[mt][nt]);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) o[mt][nt] = mfma_16x16x32_bf16(pa_lo, vb[nt], o[mt][nt]);
       }
     }
+
+    // e. hand the next tile's partial logits over
+    if (tile + 1 < ntiles) {
+      s_xchg[wv][0][lane] = snext[0];
+      s_xchg[wv][1][lane] = snext[1];
+      sacc[0] = snext[0];
+      sacc[1] = snext[1];
+    }
+    __syncthreads();  // A(tile + 1)
   }
 
-  // 5. publish per-head (m, l); write the output or this split's partials
-  if (kh == 0 && j == 0) {
+  // 5. combine the two dim halves' sums per head; write the output or this
+  //    split's partials
+  if (j == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int head = 16 * hg + 4 * g + r;
-      s_ml[head][0] = m_run[r];
-      s_ml[head][1] = l_run[r];
+      s_ml[head][kh][0] = m_run[r];
+      s_ml[head][kh][1] = l_run[r];
     }
   }
   __syncthreads();
@@ -328,14 +353,14 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int head = 16 * mt + 4 * g + r;
-        const float l = s_ml[head][1];
+        const float l = s_ml[head][0][1] + s_ml[head][1][1];
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
         float *op = out + ((int64_t)row * kH + head) * kDL + 64 * wv + j;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) op[16 * nt] = o[mt][nt][r] * inv;
       }
     if (lse != nullptr && tid < kH) {
-      const float m = s_ml[tid][0], l = s_ml[tid][1];
+      const float m = s_ml[tid][0][0], l = s_ml[tid][0][1] + s_ml[tid][1][1];
       lse[(int64_t)row * kH + tid] = l > 0.0f ? m * kLn2 + logf(l) : -INFINITY;
     }
   } else {
@@ -350,8 +375,8 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_bf16_kernel(
         for (int nt = 0; nt < 4; ++nt) op[16 * nt] = o[mt][nt][r];
       }
     if (tid < kH) {
-      ws_ml[(part * kH + tid) * 2 + 0] = s_ml[tid][0];
-      ws_ml[(part * kH + tid) * 2 + 1] = s_ml[tid][1];
+      ws_ml[(part * kH + tid) * 2 + 0] = s_ml[tid][0][0];
+      ws_ml[(part * kH + tid) * 2 + 1] = s_ml[tid][0][1] + s_ml[tid][1][1];
     }
   }
 }

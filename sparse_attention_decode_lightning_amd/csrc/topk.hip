@@ -11,8 +11,8 @@
 //  * three radix passes (11, 11 and 10 bits, most significant first) over the
 //    candidates that still match the chosen prefix find the k-th largest key
 //    tau and how many keys equal to tau must be kept ("need"); each pass is a
-//    shared LDS histogram followed by a suffix scan (wave shuffles plus one
-//    exchange of wave totals);
+//    shared LDS histogram that one wave then scans from the top, so a pass
+//    costs two barriers;
 //  * one ordered pass: each thread owns a contiguous run of candidates, counts
 //    its keys > tau and == tau, and a block-wide exclusive scan of those counts
 //    gives every kept candidate its output slot, so positions come out in
@@ -32,7 +32,7 @@ namespace {
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kChunk = 32768;  // candidates per workgroup (keys cached in LDS)
-constexpr int kBins = 2048;
+constexpr int kBinsA = 2048;   // 11-bit digits: key bits 31..21, 20..10, then 9..0
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -40,8 +40,13 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Histogram bins are padded by one word per 64, so that a lane reading 64
+// consecutive bins hits a different bank than its neighbours.
+__device__ __forceinline__ int padded(int bin) { return bin + (bin >> 6); }
+
 struct TopkShared {
-  uint32_t hist[kBins];
+  uint32_t hist_a[kBinsA + kBinsA / 64];
+  uint32_t hist_b[kBinsA + kBinsA / 64];
   uint32_t wave_tot[kTopkWaves];
   uint32_t digit, need;
 };
@@ -63,47 +68,102 @@ __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, TopkShared 
   return v + before;
 }
 
+// One wave finds, in a padded histogram of NB bins, the digit d holding the
+// need-th largest candidate: count(digit > d) < need <= count(digit >= d).
+// Lane l owns bins [NB/64 * l, NB/64 * (l+1)).
+template <int NB>
+__device__ __forceinline__ void wave_pick_digit(const uint32_t *hist, uint32_t need,
+                                                TopkShared &sh) {
+  constexpr int per = NB / 64;
+  const int lane = threadIdx.x & 63;
+  uint32_t h[per];  // the lane's bins, read once (independent loads, no bank conflicts)
+#pragma unroll
+  for (int i = 0; i < per; ++i) h[i] = hist[padded(per * lane + i)];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < per; ++i) mine += h[i];
+  // suffix sum over lanes: total of lanes >= l
+  uint32_t suf = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t u = __shfl_down(suf, off);
+    if (lane + off < 64) suf += u;
+  }
+  const uint32_t above = suf - mine;  // candidates in lanes > l
+  if (above < need && suf >= need) {
+    uint32_t acc = above, digit = 0, rest = 0;
+    bool found = false;
+#pragma unroll
+    for (int i = per - 1; i >= 0; --i) {
+      const bool here = !found && acc + h[i] >= need;
+      digit = here ? (uint32_t)(per * lane + i) : digit;
+      rest = here ? need - acc : rest;
+      found |= here;
+      acc += h[i];
+    }
+    sh.digit = digit;
+    sh.need = rest;
+  }
+}
+
 // Finds tau (the k-th largest key among keys[0..n)) and how many keys equal to
-// tau belong to the top-k. Requires n > k.
+// tau belong to the top-k. Requires n > k. Both histograms must be zero on
+// entry. Passes alternate between the two histograms so that one is cleared
+// while the other is counted.
 __device__ void radix_select(const uint32_t *keys, int n, uint32_t k, TopkShared &sh,
                              uint32_t &tau, uint32_t &need_out) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0, need = k;
-  const int shifts[3] = {21, 10, 0};
-  const uint32_t widths[3] = {11, 11, 10};
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = shifts[pass];
-    const uint32_t dmask = (1u << widths[pass]) - 1u;
-    for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += kTopkThreads) {
-      const uint32_t key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    // thread t owns digits 2047-2t and 2046-2t, so a prefix over threads is a
-    // suffix over digits
-    const int d_hi = kBins - 1 - 2 * tid, d_lo = d_hi - 1;
-    const uint32_t h_hi = sh.hist[d_hi], h_lo = sh.hist[d_lo];
-    const uint32_t incl = block_inclusive_scan(h_hi + h_lo, sh);
-    const uint32_t s_lo = incl;           // candidates with digit >= d_lo
-    const uint32_t s_hi = incl - h_lo;    // candidates with digit >= d_hi
-    if (s_hi >= need && s_hi - h_hi < need) {
-      sh.digit = (uint32_t)d_hi;
-      sh.need = need - (s_hi - h_hi);
-    } else if (s_lo >= need && s_lo - h_lo < need) {
-      sh.digit = (uint32_t)d_lo;
-      sh.need = need - (s_lo - h_lo);
-    }
-    __syncthreads();
-    prefix |= sh.digit << shift;
-    mask |= dmask << shift;
-    need = sh.need;
-    __syncthreads();
+  const int tid = threadIdx.x, wv = tid >> 6;
+  // pass 1: bits 31..21 into hist_a
+  for (int i = tid; i < n; i += kTopkThreads) atomicAdd(&sh.hist_a[padded(keys[i] >> 21)], 1u);
+  __syncthreads();
+  if (wv == 0) wave_pick_digit<kBinsA>(sh.hist_a, k, sh);
+  __syncthreads();
+  uint32_t prefix = sh.digit << 21, need = sh.need;
+  // pass 2: bits 20..10 into hist_b (zero on entry) while hist_a is cleared
+  for (int i = tid; i < kBinsA + kBinsA / 64; i += kTopkThreads) sh.hist_a[i] = 0;
+  for (int i = tid; i < n; i += kTopkThreads) {
+    const uint32_t key = keys[i];
+    if ((key >> 21) == (prefix >> 21)) atomicAdd(&sh.hist_b[padded((key >> 10) & 2047u)], 1u);
   }
-  tau = prefix;
-  need_out = need;
+  __syncthreads();
+  if (wv == 0) wave_pick_digit<kBinsA>(sh.hist_b, need, sh);
+  __syncthreads();
+  prefix |= sh.digit << 10;
+  need = sh.need;
+  // pass 3: bits 9..0 into hist_a
+  for (int i = tid; i < n; i += kTopkThreads) {
+    const uint32_t key = keys[i];
+    if ((key >> 10) == (prefix >> 10)) atomicAdd(&sh.hist_a[padded(key & 1023u)], 1u);
+  }
+  __syncthreads();
+  if (wv == 0) wave_pick_digit<kBinsA / 2>(sh.hist_a, need, sh);
+  __syncthreads();
+  tau = prefix | sh.digit;
+  need_out = sh.need;
+}
+
+// Loads n scores into LDS as order keys, with every load of a thread in
+// flight before any is converted.
+__device__ __forceinline__ void load_keys(const float *src, int n, uint32_t *keys) {
+  constexpr int kU = 8;
+  for (int base = 0; base < n; base += kU * kTopkThreads) {
+    float v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * kTopkThreads + (int)threadIdx.x;
+      v[u] = i < n ? src[i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * kTopkThreads + (int)threadIdx.x;
+      if (i < n) keys[i] = order_key(v[u]);
+    }
+  }
+}
+
+__device__ __forceinline__ void clear_hists(TopkShared &sh) {
+  for (int i = threadIdx.x; i < kBinsA + kBinsA / 64; i += kTopkThreads) sh.hist_a[i] = 0;
+  for (int i = threadIdx.x; i < kBinsA + kBinsA / 64; i += kTopkThreads) sh.hist_b[i] = 0;
 }
 
 // Writes the kept candidates' positions in candidate order: every key > tau
@@ -166,7 +226,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
   const int n = min(kChunk, n_row - c0);
   if (n <= 0) return;
   const float *src = scores + (int64_t)row * ld + c0;
-  for (int i = tid; i < n; i += kTopkThreads) s_keys[i] = order_key(src[i]);
+  clear_hists(sh);
+  load_keys(src, n, s_keys);
   __syncthreads();
   int32_t *out_pos;
   uint32_t *out_key = nullptr;
@@ -218,15 +279,30 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
   __syncthreads();
   const int n = s_start[n_chunks];
   const int64_t base = (int64_t)row * n_chunks * k;
-  for (int c = 0; c < n_chunks; ++c) {
-    const int m = s_start[c + 1] - s_start[c];
-    for (int i = tid; i < m; i += kTopkThreads)
-      s_keys[s_start[c] + i] = ws_key[base + (int64_t)c * k + i];
+  clear_hists(sh);
+  auto chunk_of = [&](int i) {
+    int c = 0;
+    while (c + 1 < n_chunks && s_start[c + 1] <= i) ++c;
+    return c;
+  };
+  constexpr int kU = 8;
+  for (int b0 = 0; b0 < n; b0 += kU * kTopkThreads) {
+    uint32_t v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = b0 + u * kTopkThreads + tid;
+      const int c = chunk_of(i);
+      v[u] = i < n ? ws_key[base + (int64_t)c * k + (i - s_start[c])] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = b0 + u * kTopkThreads + tid;
+      if (i < n) s_keys[i] = v[u];
+    }
   }
   __syncthreads();
   auto pos_of = [&](int i) -> int32_t {
-    int c = 0;
-    while (c + 1 < n_chunks && s_start[c + 1] <= i) ++c;
+    const int c = chunk_of(i);
     return ws_pos[base + (int64_t)c * k + (i - s_start[c])];
   };
   if (n <= k) {  // a single chunk already reduced to exactly k survivors
