@@ -91,6 +91,33 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Division by a runtime divisor d >= 1 as a multiply-high and a shift
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994, round-up variant): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(n, m) + n) >> l for every
+// 0 <= n < 2^31. The host fills the pair; kernels divide with two VALU ops.
+struct FastDiv {
+  uint32_t mul;
+  uint32_t shift;
+};
+
+inline FastDiv make_fast_div(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint64_t m = (((1ull << 32) * ((1ull << l) - d)) / d) + 1;
+  return FastDiv{(uint32_t)m, l};
+}
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
+  return (__umulhi(n, f.mul) + n) >> f.shift;
+}
+
+// max(x, 0) as an integer max on the bits: negative floats (and -0) have the
+// sign bit set and compare below 0 as int32, non-negative floats keep their bits.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
 // Sequence of a flattened query row: the largest b with cu_q[b] <= row.
 // cu_q is non-decreasing, so cu_q[b] <= row < cu_q[b + 1] for the result.
 __device__ __forceinline__ int find_seq(const int32_t *cu_q, int batch, int row) {

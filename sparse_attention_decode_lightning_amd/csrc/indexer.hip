@@ -16,6 +16,8 @@
 // Keys are read straight from HBM into MFMA operand registers, every key byte
 // once per query group; each lane's 16-byte loads from one key row keep all
 // of a 64-byte (bf16) or 32-byte (fp8) run in one instruction.
+#include <algorithm>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -140,6 +142,237 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_mfma_kernel(
   }
 }
 
+// Prefill path (bf16 queries and keys, head_dim 128, many queries per
+// sequence). The scores of a block of consecutive query rows form a GEMM
+// [rows x heads, 128] x [128, keys] followed by the per-head ReLU and weighted
+// head sum, and the same keys serve every row of the block. A workgroup of 8
+// waves keeps the query fragments of its rows in registers for its whole key
+// range and streams the keys through LDS in blocks of 64.
+//
+// Each wave owns 64 (query, head) rows as two 32-row M-tiles of
+// v_mfma_f32_32x32x16_bf16 (4, 2 or 1 queries for 16, 32 or 64 heads) and a
+// block is two 32-key N-tiles, 8 K-steps each. The 32x32 shape leaves room for
+// about five VALU ops under each 32-cycle MFMA, which the ReLU, weight and head
+// sum (two ops per accumulator element) fit: N-tile 0's MFMAs issue alongside
+// the previous block's N-tile 1 epilogue, N-tile 1's alongside N-tile 0's, so
+// the barrier between blocks never leaves the matrix core without work.
+//
+// LDS rows are 256 B with their 16-byte chunks XOR-swizzled by the key's low
+// bits, so the 32 keys of one B fragment spread over all bank groups. A lane's
+// head sum covers 16 or 32 of its query's heads; one permlane32 swap adds the
+// other half and leaves lane l with the score of key l of the block, so every
+// query row stores 256 contiguous bytes.
+constexpr int kPfThreads = 512;
+constexpr int kPfWaves = kPfThreads / kWave;
+constexpr int kPfKeys = 64;                              // keys per LDS block
+constexpr int kPfChunks = kPfKeys * kIdxDim * 2 / 16;    // 16-byte chunks per block
+constexpr int kPfStage = kPfChunks / kPfThreads;         // staged chunks per thread
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16_bf16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// CONTIG: the page size is a multiple of kPfKeys, so each block of 64 keys is
+// 64 consecutive rows of one page, found with one (scalar) block-table read.
+template <int H, bool CONTIG>
+__global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ cu_q, int batch, int total_q, int max_seq_len, int64_t bt_stride,
+    const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
+    const uint8_t *__restrict__ kdata, int64_t num_pages, int page_size,
+    float *__restrict__ scores, int64_t ld, int keys_per_split, FastDiv pdiv) {
+  constexpr int QW = 64 / H;           // query rows per wave
+  constexpr int QB = kPfWaves * QW;    // query rows per workgroup
+  __shared__ u32x4_t kbuf[2][kPfChunks];
+
+  const int qblk = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int lc = lane & 31, lh = lane >> 5;
+  if (b >= batch) return;
+  const int L = min(max(seq_lens[b], 0), max_seq_len);
+  const int q0 = min(max(cu_q[b], 0), total_q);
+  const int qn = min(max(cu_q[b + 1], q0), total_q) - q0;
+  const int i0 = qblk * QB;
+  if (i0 >= qn) return;
+  const int nq = min(QB, qn - i0);
+  const int t_first = L - qn + i0;
+  const int t_last = t_first + nq - 1;
+  const int kbeg = split * keys_per_split;
+  if (t_last < 0 || kbeg > t_last) return;
+  const int kend = min(kbeg + keys_per_split, t_last + 1);
+  const int nblk = (kend - kbeg + kPfKeys - 1) / kPfKeys;
+
+  // Row 32 * m + x of this wave is (query u = (32 m + x) / H, head (32 m + x) % H).
+  // A fragments: lane (lh, lc) holds row 32 * m + lc, dims 16 * s + 8 * lh .. + 8.
+  // Accumulator element 4 * i + r of M-tile m is row 32 * m + 8 * i + 4 * lh + r.
+  u32x4_t a[2][8];
+  float wr[2][16];
+  int tq[QW];
+  int64_t orow[QW];
+#pragma unroll
+  for (int u = 0; u < QW; ++u) {
+    const int qi = wv * QW + u;
+    orow[u] = (int64_t)(q0 + i0 + min(qi, nq - 1)) * ld;
+    tq[u] = qi < nq ? t_first + qi : -1;
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int xa = 32 * m + lc;
+    const int64_t rowa = q0 + i0 + min(wv * QW + xa / H, nq - 1);
+    const uint16_t *qp = q_idx + (rowa * H + xa % H) * kIdxDim + 8 * lh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) a[m][s] = ldg16(qp + 16 * s);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int x = 32 * m + 8 * (e >> 2) + 4 * lh + (e & 3);
+      const int64_t roww = q0 + i0 + min(wv * QW + x / H, nq - 1);
+      wr[m][e] = w[roww * H + x % H];
+    }
+  }
+
+  // Staging: thread tid moves chunk (tid & 15) of keys tid / 16 + 32 * i.
+  const int cw = tid & 15;
+  const int kr0 = tid >> 4;
+  const int lds_chunk = cw ^ (kr0 & 15);
+  const int64_t bt_row = (int64_t)b * bt_stride;
+  u32x4_t stage[kPfStage];
+  int btv[kPfStage];
+  auto key_pos = [&](int blk, int i) { return min(kbeg + blk * kPfKeys + kr0 + 32 * i, t_last); };
+  auto clamp_page = [&](int64_t page) {
+    return page < 0 ? (int64_t)0 : (page >= num_pages ? num_pages - 1 : page);
+  };
+  auto bt_load = [&](int blk) {
+    if constexpr (CONTIG) {
+      btv[0] = block_table[bt_row + (int)fast_div((uint32_t)(kbeg + blk * kPfKeys), pdiv)];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPfStage; ++i)
+        btv[i] = block_table[bt_row + (int)fast_div((uint32_t)key_pos(blk, i), pdiv)];
+    }
+  };
+  auto gload = [&](int blk) {
+    if constexpr (CONTIG) {
+      const int kb0 = kbeg + blk * kPfKeys;
+      const int pidx = (int)fast_div((uint32_t)kb0, pdiv);
+      const int64_t page = clamp_page(btv[0]);
+      const uint8_t *base = kdata + (page * page_size + (kb0 - pidx * page_size)) * (2 * kIdxDim);
+#pragma unroll
+      for (int i = 0; i < kPfStage; ++i)
+        stage[i] = ldg16(base + (kr0 + 32 * i) * (2 * kIdxDim) + cw * 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPfStage; ++i) {
+        const int pos = key_pos(blk, i);
+        const int in_page = pos - (int)fast_div((uint32_t)pos, pdiv) * page_size;
+        const int64_t row = clamp_page(btv[i]) * page_size + in_page;
+        stage[i] = ldg16(kdata + row * (2 * kIdxDim) + cw * 16);
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kPfStage; ++i) kbuf[buf][(kr0 + 32 * i) * 16 + lds_chunk] = stage[i];
+  };
+
+  // B fragment of N-tile n, step s: lane (lh, lc) reads key 32 n + lc, chunk 2 s + lh.
+  auto mma = [&](const u32x4_t *kb, int n, f32x16_t (&acc)[2]) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[m][e] = 0.0f;
+    const int key = 32 * n + lc;
+    u32x4_t bq[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) bq[s] = kb[key * 16 + ((2 * s + lh) ^ (key & 15))];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) acc[m] = mfma_32x32x16_bf16(a[m][s], bq[s], acc[m]);
+  };
+  // Issue order of one N-tile phase: B reads run two K-steps ahead of the
+  // MFMAs that use them, and four VALU ops of the other tile's epilogue follow
+  // each MFMA.
+  auto phase_order = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      if ((i & 1) == 0 && i / 2 + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  auto epi = [&](const f32x16_t (&acc)[2], float (&p)[QW]) {
+#pragma unroll
+    for (int u = 0; u < QW; ++u) p[u] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int u = (32 * m + 8 * (e >> 2)) / H;
+        p[u] = fmaf(wr[m][e], relu_bits(acc[m][e]), p[u]);
+      }
+  };
+  // Lanes l and l ^ 32 hold the two halves of a query's head sum for key
+  // 32 n + (l & 31); the swap pairs tile 0's upper half with tile 1's lower.
+  auto store = [&](int blk, const float (&p0)[QW], const float (&p1)[QW]) {
+    const int pos = kbeg + blk * kPfKeys + lane;
+#pragma unroll
+    for (int u = 0; u < QW; ++u) {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0[u]), __float_as_uint(p1[u]),
+                                                 false, false);
+      const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      if (pos <= tq[u] && pos < kend) scores[orow[u] + pos] = v;
+    }
+  };
+
+  bt_load(0);
+  gload(0);
+  lstore(0);
+  if (nblk > 1) {
+    bt_load(1);
+    gload(1);
+    if (nblk > 2) bt_load(2);
+  }
+  // Every prologue load has landed: the loop then waits only on its own loads.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // Block blk: N-tile 0's MFMAs with the epilogue of block blk - 1's N-tile 1
+  // (zeros before the first block, never stored), then N-tile 1's MFMAs with
+  // N-tile 0's epilogue. The issue pattern interleaves one MFMA with four VALU.
+  f32x16_t acc0[2], acc1[2];
+  float p0[QW], p1[QW];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc1[m][e] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < QW; ++u) p0[u] = 0.0f;
+  for (int blk = 0; blk < nblk; ++blk) {
+    const u32x4_t *kb = kbuf[blk & 1];
+    mma(kb, 0, acc0);
+    epi(acc1, p1);
+    phase_order();
+    if (blk > 0) store(blk - 1, p0, p1);
+    mma(kb, 1, acc1);
+    epi(acc0, p0);
+    phase_order();
+    if (blk + 1 < nblk) {
+      lstore((blk & 1) ^ 1);
+      if (blk + 2 < nblk) {
+        gload(blk + 2);
+        if (blk + 3 < nblk) bt_load(blk + 3);
+      }
+    }
+    __syncthreads();
+  }
+  epi(acc1, p1);
+  store(nblk - 1, p0, p1);
+}
+
 // Any element types and sizes: one thread per (query row, key position), fp32
 // fused multiply-adds over dims and heads.
 template <typename QT, int KDT>
@@ -192,9 +425,46 @@ hipError_t launch_mfma(const BatchArgs &bt, const void *q_idx, const float *w,
   return hipGetLastError();
 }
 
+// Workgroups that fill the chip once: the prefill grid splits each sequence's
+// key range until the query blocks times the splits reach this count.
+constexpr int kFillWorkgroups = 256;
+// Queries per sequence from which the prefill kernel takes over.
+constexpr int kPrefillMinQ = 16;
+
+template <int H>
+hipError_t launch_prefill(const BatchArgs &bt, const void *q_idx, const float *w,
+                          const CacheArgs &keys, float *scores, int64_t ld, hipStream_t stream) {
+  constexpr int QB = kPfWaves * (64 / H);
+  const int qblocks = (bt.max_q + QB - 1) / QB;
+  const int kblocks = (bt.max_seq_len + kPfKeys - 1) / kPfKeys;
+  const int64_t units = (int64_t)qblocks * bt.batch;
+  int splits = (int)std::min<int64_t>((kFillWorkgroups + units - 1) / units, kblocks);
+  splits = std::max(splits, 1);
+  const int keys_per_split = ((kblocks + splits - 1) / splits) * kPfKeys;
+  splits = (bt.max_seq_len + keys_per_split - 1) / keys_per_split;
+  if (splits > 65535 || bt.batch > 65535) return hipErrorInvalidConfiguration;
+  dim3 grid(qblocks, splits, bt.batch);
+  const FastDiv pdiv = make_fast_div((uint32_t)keys.page_size);
+  auto kernel = keys.page_size % kPfKeys == 0 ? indexer_prefill_kernel<H, true>
+                                              : indexer_prefill_kernel<H, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(kPfThreads), 0, stream, bt.block_table, bt.seq_lens,
+                     bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, bt.bt_stride,
+                     static_cast<const uint16_t *>(q_idx), w,
+                     static_cast<const uint8_t *>(keys.data), keys.num_pages, keys.page_size,
+                     scores, ld, keys_per_split, pdiv);
+  return hipGetLastError();
+}
+
 template <bool FP8>
 hipError_t dispatch_mfma(const BatchArgs &bt, const void *q_idx, const float *w, int n_heads,
                          const CacheArgs &keys, float *scores, int64_t ld, hipStream_t stream) {
+  if (!FP8 && bt.max_q >= kPrefillMinQ) {
+    switch (n_heads) {
+      case 16: return launch_prefill<16>(bt, q_idx, w, keys, scores, ld, stream);
+      case 32: return launch_prefill<32>(bt, q_idx, w, keys, scores, ld, stream);
+      default: return launch_prefill<64>(bt, q_idx, w, keys, scores, ld, stream);
+    }
+  }
   const bool multi = bt.max_q > 1;
   switch (n_heads) {
     case 16:

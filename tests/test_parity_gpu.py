@@ -24,6 +24,14 @@ SMALL_CASES = {
     "fp8_multiquery": small_variant("verify_b8_l240k", batch=2, lens=(1500, 777), topk=256),
     "bf16_prefill": small_variant("prefill_q4k_l32k", batch=1, lens=1200, q_per_seq=300,
                                   topk=256),
+    # prefill kernel: 64 heads, ragged query counts (some below one query
+    # block, one equal to its sequence), pages of 48 across 64-key blocks
+    "bf16_prefill_h64_ragged": small_variant("prefill_q4k_l32k", batch=3, lens=(900, 257, 70),
+                                             q_per_seq=(40, 17, 70), idx_heads=64,
+                                             page_size=48, topk=128),
+    # prefill kernel: 16 heads (32 rows per workgroup), pages of 16
+    "bf16_prefill_h16": small_variant("prefill_q4k_l32k", batch=2, lens=(500, 333),
+                                      q_per_seq=(33, 20), idx_heads=16, page_size=16, topk=64),
     "edge_lengths": small_variant(BF16_DECODE, batch=4, lens=(5, 1, 70, 64), q_per_seq=(1, 0, 3, 1),
                                   topk=64),
     "page_size_1": small_variant(BF16_DECODE, batch=2, lens=(130, 47), page_size=1, topk=32),
