@@ -118,15 +118,21 @@ __device__ __forceinline__ float relu_bits(float x) {
   return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
 }
 
-// Sequence of a flattened query row: the largest b with cu_q[b] <= row.
-// cu_q is non-decreasing, so cu_q[b] <= row < cu_q[b + 1] for the result.
+// Sequence of a flattened query row: the largest b < batch with
+// cu_q[b] <= row (0 if none). Wave-cooperative: every lane of the wave must be
+// active and pass the same row. Each lane tests one offset per 64-sequence
+// chunk; with non-decreasing offsets the hits form a prefix, so one load per
+// lane and a ballot replace a chain of dependent loads.
 __device__ __forceinline__ int find_seq(const int32_t *cu_q, int batch, int row) {
-  int lo = 0, hi = batch - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
+  const int lane = threadIdx.x & 63;
+  int b = 0;
+  for (int base = 0; base < batch; base += 64) {
+    const int i = base + lane;
+    const uint64_t hit = __ballot(i < batch && cu_q[i] <= row);
+    if (hit != 0ull) b = base + 63 - __clzll(hit);
+    if (hit != ~0ull) break;
   }
-  return lo;
+  return b;
 }
 
 struct RowInfo {
@@ -134,7 +140,8 @@ struct RowInfo {
   int t;  // absolute position of the row; -1 if the metadata leaves it none
 };
 
-// Sequence and causal position of a flattened query row, with every value
+// Sequence and causal position of a flattened query row (wave-cooperative,
+// as find_seq), with every value
 // clamped so malformed metadata can never index past the caller's buffers:
 // q offsets into [0, total_q], lengths into [0, max_seq_len], t <= L - 1.
 __device__ __forceinline__ RowInfo row_info(const int32_t *cu_q, const int32_t *seq_lens,

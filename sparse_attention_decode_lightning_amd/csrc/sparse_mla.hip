@@ -5,35 +5,41 @@
 // row is a 512-d latent plus a 64-d RoPE key, the key projection is absorbed
 // into the 576-d query and the value is the latent itself).
 //
-// MFMA path (bf16, 64 heads, 512 + 64): one 512-thread workgroup (8 waves)
-// owns one query row and one contiguous slice ("split") of its k index slots,
-// walked in tiles of 32 selected rows.
+// MFMA path (bf16, 64 heads, 512 + 64): one 256-thread workgroup (4 waves,
+// one per SIMD) owns one query row and one contiguous slice ("split") of its
+// k index slots, walked in tiles of 32 selected rows. Wave w owns heads
+// 16w..16w+15 for the whole slice: their logits, online softmax and the full
+// 16 x 512 output, so the waves share nothing but the row tiles.
 //  * All selected positions of the split are translated to physical rows once,
-//    up front, into an LDS table.
-//  * Gather: every selected 1152-byte row is read with coalesced 16-byte loads
-//    (wave w fetches rows 4w..4w+3 of a tile, 1024 contiguous bytes of one row
-//    per instruction from a row base in scalar registers). Tile i+2 is loaded
-//    into registers while tile i is computed, and stored into the LDS buffer
-//    tile i-1 used (two buffers; rows padded to 1168 bytes so that the MFMA
-//    operand reads below are bank-conflict free).
-//  * Logits: waves (hg, kh) and (hg, 1-kh) compute heads 16hg..16hg+15
-//    against the 32 rows over dims 288kh..288kh+287 (v_mfma_f32_16x16x32_bf16,
-//    query block in registers, operand reads one k-step ahead of the MFMAs).
-//    Each hands its partial logits to the other through LDS, so both hold the
-//    full logits and run the online softmax (base 2, scale folded with
-//    log2 e) for their 16 heads without further exchange.
-//  * PV: probabilities go to LDS as bf16 hi + lo pairs (p = hi + lo to 2^-16
-//    relative, so rounding p costs no accuracy); wave w owns output dims
-//    64w..64w+63 for all 64 heads. The value operand needs 8 consecutive rows
-//    of one dim per lane; ds_read_b64_tr_b16 delivers exactly that from the
-//    row-major tile (each 16-lane group reads a 4 x 16 block and gets it
-//    transposed), two reads per operand.
-//  * Two barriers per tile: after the partial-logit exchange and after the
-//    probabilities are written.
+//    up front, into an LDS table (invalid slots point at a valid row of the
+//    sequence and are masked), with a validity bitmask per tile.
+//  * Gather: each tile is copied by direct global-to-LDS loads, three tiles
+//    ahead of the one being computed (four LDS stages, one barrier per tile).
+//    Wave w moves rows 8w..8w+7: 8 x 1152 bytes are exactly nine 64-lane
+//    16-byte instructions. Rows are stored unpadded, their 16-byte chunks
+//    XOR-permuted by the row's low bits so that both operand read patterns
+//    below hit distinct banks.
+//  * Logits, transposed: S^T = C Q^T on v_mfma_f32_16x16x32_bf16 with tile rows
+//    on M (A operand from LDS) and the wave's 16 heads on N (the query block
+//    stays in registers for the whole slice). Each lane then holds one head's
+//    logits for 8 rows: the softmax maximum and sum are in-lane, plus two
+//    permlane swaps for the tile maximum across the four lane groups.
+//  * The probabilities of a lane are already the A operand of the PV product
+//    (head on M, the 8 rows as its k-slots), split as p = hi + lo in bf16 (two
+//    MFMAs per value operand) so that rounding p costs no accuracy; the value
+//    operand needs 8 rows of one dim per lane, which ds_read_b64_tr_b16
+//    delivers from the row-major tile, two reads per operand.
+//  * Softmax in base 2 with the scale folded into one multiply-add, against a
+//    reference maximum per head fixed by its first valid tile. Later logits
+//    may exceed it by up to kHeadroom (p <= 2^kHeadroom keeps every sum
+//    finite); a tile beyond that restarts the split with a higher reference.
+//    The accumulated output is thus only ever written by MFMAs in the loop.
 //  * Workgroups are numbered so that all splits of a row land on the same XCD
 //    (workgroups are dispatched round-robin over the 8 XCDs), so the row's
 //    query block is fetched from HBM once and then served by that XCD's L2.
 //  * Splits of a row are merged by a log-sum-exp combine kernel.
+#include <type_traits>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -48,31 +54,33 @@ constexpr int kDL = 512;
 constexpr int kDR = 64;
 constexpr int kD = kDL + kDR;               // 576
 constexpr int kRowBytes = kD * 2;           // 1152
-constexpr int kRowStride = kRowBytes + 16;  // LDS row stride (bytes)
 constexpr int kTileN = 32;
-constexpr int kMlaThreads = 512;
-constexpr int kPStride = kTileN * 2 + 16;  // bytes per head row of P
-constexpr int kSteps = kD / 32;            // 18 MFMA k-steps for the logits
-constexpr int kHalfSteps = kSteps / 2;     // each wave of a head group covers half the dims
+constexpr int kTileBytes = kTileN * kRowBytes;
+constexpr int kMlaThreads = 256;
+constexpr int kMlaWaves = kMlaThreads / kWave;
+constexpr int kStages = 4;                  // LDS row tiles: one computed, three landing
+constexpr int kSteps = kD / 32;             // 18 MFMA k-steps for the logits
+constexpr int kGatherInsts = kTileBytes / kMlaWaves / (kWave * 16);  // 9 per wave per tile
 constexpr int kMinRowsPerSplit = 128;
 constexpr int kXcds = 8;
 constexpr int kMaxRowsPerSplit = 2048;
 constexpr int kMaxSplits = 64;
-constexpr int kRowBufs = 3;  // row tiles in LDS: computed, next, landing
-constexpr float kLazy = 8.0f;  // log2 headroom before the reference maximum moves
+constexpr float kHeadroom = 64.0f;  // log2 headroom of p above 1 before a restart
+constexpr uint32_t kInvalid = 0x80000000u;  // row-table flag: slot masked
 
-// Row <-> MFMA k-slot map of the PV contraction. Lane group g of the value
-// operand reads rows 16L + 8(g&1) + (g>>1) + 2e (e < 4) in transposed load L,
-// so each 32-lane half of a ds_read_b64_tr_b16 touches only even or only odd
-// rows and the 1168-byte row stride keeps its banks disjoint. The
-// probabilities are stored in the same k order.
-__device__ __forceinline__ int pv_slot(int row) {
-  const int L = row >> 4, r = row & 15;
-  const int g = 2 * (r & 1) + (r >> 3);
-  return 8 * g + 4 * L + ((r & 7) >> 1);
+static_assert(kGatherInsts * kWave * 16 * kMlaWaves == kTileBytes, "gather covers a tile");
+
+// Tile row held by lane x of M-tile m of the logits product: the even rows of
+// the 16-row half, then the odd ones. Each 32-lane half of a transposed value
+// read then touches rows of one parity, whose chunks fill all 64 banks.
+__device__ __forceinline__ int tile_row(int m, int x) { return 16 * m + 2 * (x & 7) + (x >> 3); }
+
+// Chunk c (16 bytes) of tile row r is stored at chunk chunk_swz(c, r) of the
+// row; the map is its own inverse. Latent chunks are XOR-ed with the row's low
+// 4 bits, the 8 RoPE chunks with bits 1..3 (within 64..71).
+__device__ __forceinline__ int chunk_swz(int c, int r) {
+  return c < 64 ? (c ^ (r & 15)) : (64 + ((c - 64) ^ ((r >> 1) & 7)));
 }
-
-static_assert(kTileN == 32 && kMlaThreads == 512, "gather map below assumes 4 rows per wave");
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -81,27 +89,60 @@ typedef short __attribute__((address_space(3))) *lds_i16_ptr;
 
 // Lane i of each 16-lane group receives column i of the 4 x 16 block of
 // 16-bit values whose row e is supplied (4 values each) by lanes 4e..4e+3.
-__device__ __forceinline__ uint2 lds_read_tr16(const void *p) {
+__device__ __forceinline__ uint2 lds_read_tr16(const __attribute__((address_space(3))) void *p) {
   const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4_t *)((lds_i16_ptr)(const_cast<void *>(p))));
+      (__attribute__((address_space(3))) i16x4_t *)(const_cast<__attribute__((address_space(3))) void *>(p)));
   return __builtin_bit_cast(uint2, v);
 }
 
-__global__ __launch_bounds__(kMlaThreads) void sparse_mla_bf16_kernel(
+// Direct global-to-LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds + 16 l (lds wave-uniform). Issued as inline assembly so the compiler's
+// automatic waits ignore it: its completion is awaited only by the explicit
+// vmcnt waits before the tile barriers (the compiler's per-buffer tracking of
+// such copies does not survive the tile loop's back edge, and would stall
+// every tile on the copies three tiles ahead).
+__device__ __forceinline__ void lds_load16(const void *src, const __attribute__((address_space(3))) void *lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+// Maximum over the four 16-lane groups (lanes with equal lane % 16).
+__device__ __forceinline__ float group4_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+__device__ __forceinline__ float group4_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+__global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ cu_q, int batch, int total_q, int max_seq_len, int64_t bt_stride,
     const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv, int64_t num_pages,
     int page_size, const int32_t *__restrict__ indices, int k, int n_splits, int rows_per_split,
     float scale_log2, float *__restrict__ out, float *__restrict__ lse,
     float *__restrict__ ws_acc, float *__restrict__ ws_ml) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_rows[kRowBufs][kTileN * kRowStride];
-  __shared__ __attribute__((aligned(16))) uint8_t s_phi[kH * kPStride];
-  __shared__ __attribute__((aligned(16))) uint8_t s_plo[kH * kPStride];
-  __shared__ f32x4_t s_xchg[8][2][kWave];  // partial logits handed to the other dim half
-  __shared__ float s_alpha[kH];
-  __shared__ float s_ml[kH][2][2];  // per head, per dim half: (m, l)
-  __shared__ int s_rescale[2];      // some head's reference max moved (tile parity)
-  __shared__ __attribute__((aligned(16))) int32_t s_rowid[kMaxRowsPerSplit + kTileN];
+  // four separate stage arrays (not one indexed array), so that reads of one
+  // stage are not ordered behind the direct loads still landing in the others
+  __shared__ __attribute__((aligned(1024))) uint8_t s_st0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_st1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_st2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_st3[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t s_rowid[kMaxRowsPerSplit + kTileN];
+  __shared__ uint32_t s_vmask[kMaxRowsPerSplit / kTileN + 1];
+  __shared__ float s_ml[kH][2];
+  __shared__ int s_over[kMlaWaves];
 
   // XCD-aware numbering: block id = ((row / 8) * n_splits + split) * 8 + row % 8
   const int xcd = blockIdx.x % kXcds;
@@ -112,7 +153,6 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_bf16_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, j = lane & 15;
-  const int hg = wv & 3, kh = wv >> 2;
 
   const RowInfo ri = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row);
   const int b = ri.b, t = ri.t;
@@ -121,262 +161,313 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_bf16_kernel(
   const int nrows = max(0, slot_end - slot_begin);
   const int ntiles = (nrows + kTileN - 1) / kTileN;
   const int32_t *idx_row = indices + (int64_t)row * k;
-  auto rowid_of = [&](int i) -> int32_t {  // physical row of slot i of the split, or -1
-    if (i >= nrows) return -1;
-    const int pos = idx_row[slot_begin + i];
-    if (pos < 0 || pos > t) return -1;
-    return (int32_t)paged_row(block_table, bt_stride, b, pos, page_size, num_pages);
-  };
+  // A valid row to load in place of masked slots (position 0 of the sequence).
+  const uint32_t safe_row =
+      t >= 0 ? (uint32_t)paged_row(block_table, bt_stride, b, 0, page_size, num_pages) : 0u;
 
-  // Query block of heads 16hg.. over dim half kh: lane (g, i) holds head
-  // 16hg + i, dims 288kh + 32s + 8g .. +8.
-  u32x4_t qf[kHalfSteps];
+  // Query block of heads 16wv..16wv+15, the B operand of the logits: lane
+  // (g, j) holds head 16wv + j, dims 32s + 8g .. +8.
+  u32x4_t qf[kSteps];
   {
-    const uint16_t *qp = q + ((int64_t)row * kH + 16 * hg + j) * kD + 288 * kh + 8 * g;
+    const uint16_t *qp = q + ((int64_t)row * kH + 16 * wv + j) * kD + 8 * g;
 #pragma unroll
-    for (int s = 0; s < kHalfSteps; ++s) qf[s] = ldg16(qp + 32 * s);
+    for (int s = 0; s < kSteps; ++s) qf[s] = ldg16(qp + 32 * s);
   }
 
-  // Gather map of a 32-row tile (72 chunks of 16 bytes per row): wave wv owns
-  // rows 4wv..4wv+3; chunks 0..63 of row 4wv+m go to lane = chunk, chunks
-  // 64..71 of row 4wv + lane/8 to lanes 0..31.
-  u32x4_t buf[5];
-  auto load_rows = [&](int r0, int r1, int r2, int r3) {
-    const int rids[4] = {r0, r1, r2, r3};
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      buf[m] = rids[m] >= 0 ? ldg16(kv + (int64_t)rids[m] * kRowBytes + 16 * lane)
-                            : u32x4_t{0u, 0u, 0u, 0u};
-    const int q4 = lane >> 3;
-    const int r5 = q4 == 0 ? r0 : (q4 == 1 ? r1 : (q4 == 2 ? r2 : r3));
-    buf[4] = (lane < 32 && r5 >= 0) ? ldg16(kv + (int64_t)r5 * kRowBytes + 16 * (64 + (lane & 7)))
-                                    : u32x4_t{0u, 0u, 0u, 0u};
-  };
-  auto issue_loads = [&](int tile) {
-    const int4 rid4 = *reinterpret_cast<const int4 *>(&s_rowid[tile * kTileN + 4 * wv]);
-    load_rows(__builtin_amdgcn_readfirstlane(rid4.x), __builtin_amdgcn_readfirstlane(rid4.y),
-              __builtin_amdgcn_readfirstlane(rid4.z), __builtin_amdgcn_readfirstlane(rid4.w));
-  };
-  auto store_tile = [&](int tb) {
-    uint8_t *base = s_rows[tb] + (4 * wv) * kRowStride;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      *reinterpret_cast<u32x4_t *>(base + m * kRowStride + 16 * lane) = buf[m];
-    if (lane < 32)
-      *reinterpret_cast<u32x4_t *>(base + (lane >> 3) * kRowStride + 16 * (64 + (lane & 7))) =
-          buf[4];
-  };
-  // partial logits of heads 16hg + 4g + r against rows 16nt + j of a tile,
-  // dims of half kh, with operand reads one k-step ahead of the MFMAs
-  auto logits = [&](int tb, f32x4_t (&acc)[2]) {
-    const uint8_t *rp = s_rows[tb] + j * kRowStride + 576 * kh + 16 * g;
-    u32x4_t bcur[2], bnext[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      bcur[nt] = *reinterpret_cast<const u32x4_t *>(rp + nt * 16 * kRowStride);
-    }
-#pragma unroll
-    for (int s = 0; s < kHalfSteps; ++s) {
-      if (s + 1 < kHalfSteps) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          bnext[nt] = *reinterpret_cast<const u32x4_t *>(rp + nt * 16 * kRowStride + 64 * (s + 1));
-      }
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma_16x16x32_bf16(qf[s], bcur[nt], acc[nt]);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) bcur[nt] = bnext[nt];
-    }
-  };
-
-  // ---- prologue: tile 0 is gathered before the full row table exists ----
-  if (ntiles > 0) {
-    const int mine = lane < 4 ? rowid_of(4 * wv + lane) : -1;
-    load_rows(__builtin_amdgcn_readlane(mine, 0), __builtin_amdgcn_readlane(mine, 1),
-              __builtin_amdgcn_readlane(mine, 2), __builtin_amdgcn_readlane(mine, 3));
-  }
-  // translate every selected position of the split once (padding to whole
-  // tiles with -1), so the tile loop never waits on index or block-table reads
-  for (int i = tid; i < ntiles * kTileN; i += kMlaThreads) s_rowid[i] = rowid_of(i);
-  if (tid < 2) s_rescale[tid] = 0;
-
-  f32x4_t o[4][4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) o[mt][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  // m_run is each head's reference maximum: probabilities are 2^(x - m_run),
-  // and m_run only moves (with a rescale of everything accumulated so far)
-  // when a logit exceeds it by more than kLazy, so p <= 2^kLazy. l_run sums
-  // the probabilities of this wave's 16 rows of every tile.
-  float m_run[4], l_run[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m_run[r] = -INFINITY;
-    l_run[r] = 0.0f;
-  }
-
-  f32x4_t sacc[2], snext[2];
-  if (ntiles > 0) {
-    store_tile(0);
-    __syncthreads();  // row table and tile 0 visible
-    if (ntiles > 1) issue_loads(1);
-    logits(0, sacc);
-    if (ntiles > 1) {
-      store_tile(1);
-      if (ntiles > 2) issue_loads(2);
-    }
-    s_xchg[wv][0][lane] = sacc[0];
-    s_xchg[wv][1][lane] = sacc[1];
-  }
-  __syncthreads();  // A(0): partials of tile 0 and tile 1's rows visible
-
-  for (int tile = 0; tile < ntiles; ++tile) {
-    // a. logits of the next tile start in the matrix pipe while this tile's
-    //    softmax runs on the vector units
-    if (tile + 1 < ntiles) logits((tile + 1) % kRowBufs, snext);
-
-    // b. full logits and online softmax of this wave's 16 heads; both waves of
-    //    a head group see all 32 rows (same maximum), wave kh owns rows 16kh + j
-    float x[2][4];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const f32x4_t full = sacc[nt] + s_xchg[wv ^ 4][nt][lane];
-      const bool valid = s_rowid[tile * kTileN + 16 * nt + j] >= 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[nt][r] = valid ? full[r] * scale_log2 : -INFINITY;
-    }
-    if (tid == 0) s_rescale[(tile + 1) & 1] = 0;  // its last reader was PV(tile - 1)
-    float pmine[4];
-    bool moved = false;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int head = 16 * hg + 4 * g + r;
-      const float tmax = row16_max(fmaxf(x[0][r], x[1][r]));
-      const bool up = tmax > m_run[r] + kLazy;  // false while the tile is all padding
-      const float m_new = up ? tmax : m_run[r];
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = up ? fast_exp2(m_run[r] - m_use) : 1.0f;
-      const float p = fast_exp2((kh == 0 ? x[0][r] : x[1][r]) - m_use);
-      l_run[r] = l_run[r] * alpha + row16_sum(p);
-      m_run[r] = m_new;
-      moved |= up;
-      if (kh == 0 && j == 0) s_alpha[head] = alpha;
-      pmine[r] = p;
-    }
-    if (kh == 0 && __ballot(moved) != 0 && lane == 0) s_rescale[tile & 1] = 1;
-    {
-      // p = hi + lo, both bf16 (round to nearest even on the conversion unit)
-      const int slot = pv_slot(16 * kh + j);
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const f32x2_t pp = {pmine[r], pmine[r + 1]};
-        const bf16x2_t hi = __builtin_convertvector(pp, bf16x2_t);
-        const f32x2_t hf = __builtin_convertvector(hi, f32x2_t);
-        const bf16x2_t lo = __builtin_convertvector(pp - hf, bf16x2_t);
-        const int head = 16 * hg + 4 * g + r;
-        reinterpret_cast<__bf16 *>(s_phi + head * kPStride)[slot] = hi.x;
-        reinterpret_cast<__bf16 *>(s_phi + (head + 1) * kPStride)[slot] = hi.y;
-        reinterpret_cast<__bf16 *>(s_plo + head * kPStride)[slot] = lo.x;
-        reinterpret_cast<__bf16 *>(s_plo + (head + 1) * kPStride)[slot] = lo.y;
+  // Row table: physical row of every slot of the split, masked slots flagged.
+  for (int base = 0; base < ntiles * kTileN; base += kMlaThreads) {
+    const int i = base + tid;
+    bool valid = false;
+    uint32_t rid = safe_row;
+    if (i < nrows) {
+      const int pos = idx_row[slot_begin + i];
+      if (pos >= 0 && pos <= t) {
+        valid = true;
+        rid = (uint32_t)paged_row(block_table, bt_stride, b, pos, page_size, num_pages);
       }
     }
-
-    // c. the tile after next lands in the buffer PV(tile - 1) used
-    if (tile + 2 < ntiles) {
-      store_tile((tile + 2) % kRowBufs);
-      if (tile + 3 < ntiles) issue_loads(tile + 3);
+    if (i < ntiles * kTileN) s_rowid[i] = valid ? rid : (rid | kInvalid);
+    const uint64_t vb = __ballot(valid && i < ntiles * kTileN);
+    if (lane == 0 && i < ntiles * kTileN) {
+      s_vmask[i / kTileN] = (uint32_t)vb;
+      if (i + kTileN < ntiles * kTileN) s_vmask[i / kTileN + 1] = (uint32_t)(vb >> 32);
     }
-    __syncthreads();  // B(tile): probabilities and rescale factors visible
-
-    // d. rescale (only when a reference maximum moved) and accumulate P.V for
-    //    dims 64wv .. +64, all heads, K = 32 rows
-    if (s_rescale[tile & 1]) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float al = s_alpha[16 * mt + 4 * g + r];
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) o[mt][nt][r] *= al;
-        }
-    }
-    {
-      const uint8_t *rows = s_rows[tile % kRowBufs];
-      // lane (g, i) of transposed load L reads row 16L + 8(g&1) + (g>>1) + 2(i>>2)
-      const uint8_t *vbase = rows + (8 * (g & 1) + (g >> 1) + 2 * (j >> 2)) * kRowStride +
-                             (64 * wv + 4 * (j & 3)) * 2;
-      u32x4_t vb[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const uint2 v0 = lds_read_tr16(vbase + 32 * nt);
-        const uint2 v1 = lds_read_tr16(vbase + 16 * kRowStride + 32 * nt);
-        vb[nt] = u32x4_t{v0.x, v0.y, v1.x, v1.y};
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int poff = (16 * mt + j) * kPStride + 16 * g;
-        const u32x4_t pa_hi = *reinterpret_cast<const u32x4_t *>(s_phi + poff);
-        const u32x4_t pa_lo = *reinterpret_cast<const u32x4_t *>(s_plo + poff);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) o[mt][nt] = mfma_16x16x32_bf16(pa_hi, vb[nt], o[mt][nt]);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) o[mt][nt] = mfma_16x16x32_bf16(pa_lo, vb[nt], o[mt][nt]);
-      }
-    }
-
-    // e. hand the next tile's partial logits over
-    if (tile + 1 < ntiles) {
-      s_xchg[wv][0][lane] = snext[0];
-      s_xchg[wv][1][lane] = snext[1];
-      sacc[0] = snext[0];
-      sacc[1] = snext[1];
-    }
-    __syncthreads();  // A(tile + 1)
   }
 
-  // 5. combine the two dim halves' sums per head; write the output or this
-  //    split's partials
-  if (j == 0) {
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  auto stage = [&](auto st) -> lds_u8 * {
+    constexpr int ST = decltype(st)::value;
+    if constexpr (ST == 0) return (lds_u8 *)s_st0;
+    else if constexpr (ST == 1) return (lds_u8 *)s_st1;
+    else if constexpr (ST == 2) return (lds_u8 *)s_st2;
+    else return (lds_u8 *)s_st3;
+  };
+  // Gather map: instruction n of wave wv moves chunks 64n..64n+63 of the 576
+  // chunks of rows 8wv..8wv+7; lane l's chunk is row 8wv + (64n+l)/72, stored
+  // chunk (64n+l)%72, fetched from that row's chunk chunk_swz(., row). The
+  // row is one of two known to the instruction: 64n/72, or the next from lane
+  // 72(64n/72 + 1) - 64n on.
+  uint32_t goff[kGatherInsts];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int head = 16 * hg + 4 * g + r;
-      s_ml[head][kh][0] = m_run[r];
-      s_ml[head][kh][1] = l_run[r];
+  for (int n = 0; n < kGatherInsts; ++n) {
+    const int qc = 64 * n + lane;
+    const int rl = qc / 72, lc = qc % 72;
+    goff[n] = (uint32_t)(16 * chunk_swz(lc, 8 * wv + rl));
+  }
+  auto gather = [&](auto st, int tile) {
+    lds_u8 *dst = stage(st) + 8 * wv * kRowBytes;
+    const u32x4_t ra = *reinterpret_cast<const u32x4_t *>(s_rowid + tile * kTileN + 8 * wv);
+    const u32x4_t rb = *reinterpret_cast<const u32x4_t *>(s_rowid + tile * kTileN + 8 * wv + 4);
+    uint32_t rid[9];
+    rid[0] = __builtin_amdgcn_readfirstlane(ra.x) & ~kInvalid;
+    rid[1] = __builtin_amdgcn_readfirstlane(ra.y) & ~kInvalid;
+    rid[2] = __builtin_amdgcn_readfirstlane(ra.z) & ~kInvalid;
+    rid[3] = __builtin_amdgcn_readfirstlane(ra.w) & ~kInvalid;
+    rid[4] = __builtin_amdgcn_readfirstlane(rb.x) & ~kInvalid;
+    rid[5] = __builtin_amdgcn_readfirstlane(rb.y) & ~kInvalid;
+    rid[6] = __builtin_amdgcn_readfirstlane(rb.z) & ~kInvalid;
+    rid[7] = __builtin_amdgcn_readfirstlane(rb.w) & ~kInvalid;
+    rid[8] = rid[7];
+#pragma unroll
+    for (int n = 0; n < kGatherInsts; ++n) {
+      constexpr int kq[kGatherInsts] = {0, 0, 1, 2, 3, 4, 5, 6, 7};
+      const int q0 = (64 * n) / 72;
+      const int split_lane = 72 * (q0 + 1) - 64 * n;
+      const uint32_t r = lane < split_lane ? rid[q0] : rid[q0 + 1];
+      (void)kq;
+      const uint8_t *src = kv + (int64_t)r * kRowBytes + goff[n];
+      lds_load16(src, dst + 1024 * n);
     }
+  };
+
+  // Operand offsets inside a tile (loop-invariant). Logits A operand: lane
+  // (g, i) reads tile row tile_row(m, i), chunk 4s + g; M-tile 1 is 16 rows
+  // further with the same permutation. Latent steps s use a_lat[s & 3] plus
+  // 256 (s >> 2); the two RoPE steps use a_rope[s - 16].
+  const int ar = tile_row(0, j);
+  uint32_t a_lat[4], a_rope[2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) a_lat[s] = ar * kRowBytes + 16 * chunk_swz(4 * s + g, ar);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) a_rope[s] = ar * kRowBytes + 16 * chunk_swz(64 + 4 * s + g, ar);
+  // Value operand: lane (g, j), e = j / 4: transposed read L covers rows
+  // tile_row(L, 4g + e), dims 4(j & 3) .. +4 of the 16-dim tile nt. Tile nt
+  // uses v_off[nt & 7] plus 256 (nt >> 3); read L = 1 is 16 rows further.
+  const int vr = tile_row(0, 4 * g + (j >> 2));
+  uint32_t v_off[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    v_off[c] = vr * kRowBytes + 16 * ((2 * c + ((j & 3) >> 1)) ^ (vr & 15)) + 8 * (j & 1);
+  // Rows of this lane's 8 logits: value (m, r) is tile row tile_row(m, 4g + r).
+  int lrow[2][4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lrow[m][r] = tile_row(m, 4 * g + r);
+
+  f32x4_t o[32];
+#pragma unroll
+  for (int nt = 0; nt < 32; ++nt) o[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY, l_run = 0.0f;  // head 16wv + j; l_run covers this lane's rows
+  bool overflow = false;
+
+  if (tid < kMlaWaves) s_over[tid] = 0;
+  // every compiler-visible load (query block, row table) has landed before the
+  // first direct copies, which the compiler does not count
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  __syncthreads();  // row table visible
+
+  auto step = [&](auto st, int tile) -> bool {
+    constexpr int ST = decltype(st)::value;
+    // this wave's loads of `tile` have landed (later tiles may be in flight)
+    const int ahead = min(ntiles - 1 - tile, kStages - 2);
+    // (s_waitcnt fields: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8;
+    // lgkmcnt 0 also completes this wave's LDS stores, e.g. the restart flag)
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0070 | ((2 * kGatherInsts) & 15) | (((2 * kGatherInsts) >> 4) << 14));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0070 | (kGatherInsts & 15) | ((kGatherInsts >> 4) << 14));
+    else __builtin_amdgcn_s_waitcnt(0x0070);
+    // Barrier with no release fence: the wait above already covers this
+    // wave's part of `tile`, and a release fence would also wait for the
+    // later tiles' loads. Every wave's part of `tile` is visible after it, and
+    // every wave is done with the stage of tile - 1.
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if ((s_over[0] | s_over[1] | s_over[2] | s_over[3]) != 0) return true;  // an earlier tile overflowed
+    if (tile + kStages - 1 < ntiles) gather(std::integral_constant<int, (ST + kStages - 1) % kStages>{}, tile + kStages - 1);
+
+    const uint32_t vmask = s_vmask[tile];
+    if (vmask == 0u) return false;
+    const lds_u8 *tb = stage(st);
+
+    // logits (transposed): acc[m][r] = S[head 16wv + j][row lrow[m][r]], A
+    // operands read one k-step ahead of the MFMAs
+    f32x4_t acc[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+    auto a_off = [&](int s_) -> uint32_t {
+      return s_ < 16 ? a_lat[s_ & 3] + 256 * (s_ >> 2) : a_rope[s_ - 16];
+    };
+    // A operands run kAhead k-steps ahead of their MFMAs
+    constexpr int kAhead = 4;
+    u32x4_t abuf[kSteps][2];
+#pragma unroll
+    for (int s_ = 0; s_ < kAhead; ++s_)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        abuf[s_][m] = *(const __attribute__((address_space(3))) u32x4_t *)(tb + a_off(s_) + m * 16 * kRowBytes);
+#pragma unroll
+    for (int s_ = 0; s_ < kSteps; ++s_) {
+      if (s_ + kAhead < kSteps) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          abuf[s_ + kAhead][m] = *(const __attribute__((address_space(3))) u32x4_t *)(
+              tb + a_off(s_ + kAhead) + m * 16 * kRowBytes);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) acc[m] = mfma_16x16x32_bf16(abuf[s_][m], qf[s_], acc[m]);
+    }
+    // issue order: 2 * kAhead operand reads, then one read per MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * (kSteps - kAhead); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
+    if (vmask != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (!((vmask >> lrow[m][r]) & 1u)) acc[m][r] = -INFINITY;
+    }
+    // softmax of head 16wv + j in base 2 against a reference maximum m_run
+    // fixed by the head's first valid tile: p = 2^(x - m_run). A later tile
+    // may exceed it by up to kHeadroom (p <= 2^kHeadroom keeps every sum
+    // finite); beyond that the whole split restarts with a higher reference,
+    // so the accumulated output is never rescaled in the loop.
+    float mx = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
+                     fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
+    mx = group4_max(mx) * scale_log2;
+    m_run = m_run == -INFINITY ? mx : m_run;
+    const bool over = mx > m_run + kHeadroom;
+    m_run = over ? mx : m_run;  // per lane: a restarted pass starts from here
+    overflow |= over;
+    // every lane writes the same word, so no branch splits the tile's code;
+    // the flag is read by all waves after the next barrier (a restarted
+    // split discards whatever this tile accumulates)
+    s_over[wv] = __ballot(overflow) != 0ull ? 1 : 0;
+    float p[2][4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[m][r] = fast_exp2(fmaf(acc[m][r], scale_log2, -m_run));
+        l_run += p[m][r];
+      }
+    // P as the A operand of PV: head j, k-slots 8g + 4m + r <-> rows lrow[m][r].
+    // p = hi + lo in bf16 to 2^-16 relative: bf16 rounding of p alone (2^-9)
+    // is too coarse for rows that attend to only a few positions.
+    u32x4_t pa, pl;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t hi = pack_bf16x2(p[m][2 * h], p[m][2 * h + 1]);
+        const float r0 = p[m][2 * h] - __uint_as_float(hi << 16);
+        const float r1 = p[m][2 * h + 1] - __uint_as_float(hi & 0xFFFF0000u);
+        pa[2 * m + h] = hi;
+        pl[2 * m + h] = pack_bf16x2(r0, r1);
+      }
+    // value operands read one tile ahead of their MFMA
+    auto vread = [&](int nt) -> u32x4_t {
+      const lds_u8 *vp = tb + v_off[nt & 7] + 256 * (nt >> 3);
+      const uint2 v0 = lds_read_tr16(vp);
+      const uint2 v1 = lds_read_tr16(vp + 16 * kRowBytes);
+      return u32x4_t{v0.x, v0.y, v1.x, v1.y};
+    };
+    // value operands run kVAhead tiles ahead of their MFMAs
+    constexpr int kVAhead = 4;
+    u32x4_t vbuf[32];
+#pragma unroll
+    for (int nt = 0; nt < kVAhead; ++nt) vbuf[nt] = vread(nt);
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) {
+      if (nt + kVAhead < 32) vbuf[nt + kVAhead] = vread(nt + kVAhead);
+      o[nt] = mfma_16x16x32_bf16(pa, vbuf[nt], o[nt]);
+      o[nt] = mfma_16x16x32_bf16(pl, vbuf[nt], o[nt]);
+    }
+    // issue order: the first 2 * kVAhead value reads overlap the softmax
+    // above; then two reads per pair of MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 40, 0);
+#pragma unroll
+    for (int i = 0; i < 32 - kVAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kVAhead, 0);
+    return false;
+  };
+
+  // Passes over the split: normally one. A pass that meets an overflowing
+  // tile is abandoned by every wave at the next barrier (the flag is read
+  // after it), its loads are drained, and the split is walked again.
+  for (;;) {
+    if (0 < ntiles) gather(std::integral_constant<int, 0>{}, 0);
+    if (1 < ntiles) gather(std::integral_constant<int, 1>{}, 1);
+    if (2 < ntiles) gather(std::integral_constant<int, 2>{}, 2);
+    bool restart = false;
+    for (int tile = 0; tile < ntiles && !restart; tile += kStages) {
+      restart = step(std::integral_constant<int, 0>{}, tile);
+      if (!restart && tile + 1 < ntiles) restart = step(std::integral_constant<int, 1>{}, tile + 1);
+      if (!restart && tile + 2 < ntiles) restart = step(std::integral_constant<int, 2>{}, tile + 2);
+      if (!restart && tile + 3 < ntiles) restart = step(std::integral_constant<int, 3>{}, tile + 3);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no direct load of this pass in flight
+    __syncthreads();
+    if ((s_over[0] | s_over[1] | s_over[2] | s_over[3]) == 0) break;
+    __syncthreads();  // every wave has read the flags
+    if (tid < kMlaWaves) s_over[tid] = 0;
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) o[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    l_run = 0.0f;
+    overflow = false;
+    __syncthreads();
+  }
+
+  // (m, l) of head 16wv + j: every lane group holds the same m; l is summed
+  // over the groups' rows. O rows of lane (g, j) are heads 16wv + 4g + r.
+  const float l_tot = group4_sum(l_run);
+  if (g == 0) {
+    s_ml[16 * wv + j][0] = m_run;
+    s_ml[16 * wv + j][1] = l_tot;
   }
   __syncthreads();
   if (n_splits == 1) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int r = 0; r < 4; ++r) {
+      const int head = 16 * wv + 4 * g + r;
+      const float l = s_ml[head][1];
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      float *op = out + ((int64_t)row * kH + head) * kDL + j;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int head = 16 * mt + 4 * g + r;
-        const float l = s_ml[head][0][1] + s_ml[head][1][1];
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        float *op = out + ((int64_t)row * kH + head) * kDL + 64 * wv + j;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) op[16 * nt] = o[mt][nt][r] * inv;
-      }
+      for (int nt = 0; nt < 32; ++nt) op[16 * nt] = o[nt][r] * inv;
+    }
     if (lse != nullptr && tid < kH) {
-      const float m = s_ml[tid][0][0], l = s_ml[tid][0][1] + s_ml[tid][1][1];
+      const float m = s_ml[tid][0], l = s_ml[tid][1];
       lse[(int64_t)row * kH + tid] = l > 0.0f ? m * kLn2 + logf(l) : -INFINITY;
     }
   } else {
     const int64_t part = (int64_t)row * n_splits + split;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int r = 0; r < 4; ++r) {
+      const int head = 16 * wv + 4 * g + r;
+      float *op = ws_acc + (part * kH + head) * kDL + j;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int head = 16 * mt + 4 * g + r;
-        float *op = ws_acc + (part * kH + head) * kDL + 64 * wv + j;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) op[16 * nt] = o[mt][nt][r];
-      }
+      for (int nt = 0; nt < 32; ++nt) op[16 * nt] = o[nt][r];
+    }
     if (tid < kH) {
-      ws_ml[(part * kH + tid) * 2 + 0] = s_ml[tid][0][0];
-      ws_ml[(part * kH + tid) * 2 + 1] = s_ml[tid][0][1] + s_ml[tid][1][1];
+      ws_ml[(part * kH + tid) * 2 + 0] = s_ml[tid][0];
+      ws_ml[(part * kH + tid) * 2 + 1] = s_ml[tid][1];
     }
   }
 }

@@ -314,6 +314,174 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
   ordered_emit(s_keys, n, tau, need, sh, pos_of, out, nullptr);
 }
 
+// Rows of at most R * 1024 candidates (every decode row of a few thousand
+// tokens): thread tid holds candidates u * 1024 + tid (u < R) as keys in
+// registers, so the three radix passes read no LDS but their histograms. Bin
+// b of a histogram sits at word b + 4 * (b / 32): the picking wave's lane l
+// owns bins [32 l, 32 l + 32) and reads them with 16-byte loads that no
+// other lane of its group of eight shares a bank with. The ordered emit needs
+// no contiguous runs: positions run u-major, then wave, then lane, so wave
+// ballots of (key > tau) and (key == tau) per u, one scan of the R * 16 packed
+// per-wave counts and a popcount below the lane give every kept candidate its
+// slot in ascending position order.
+constexpr int kRegBinsWords = kBinsA / 32 * 36;
+
+__device__ __forceinline__ int reg_bin(uint32_t b) { return (int)(b + 4 * (b >> 5)); }
+
+struct alignas(16) TopkRegShared {
+  uint32_t hist[2][kRegBinsWords];
+  uint32_t cnt[16 * 16];
+  uint32_t digit, need;
+};
+
+// Suffix sum over the 64 lanes: lane l gets the total of lanes >= l.
+__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t u = __shfl_down(v, off);
+    if (lane + off < 64) v += u;
+  }
+  return v;
+}
+
+// One wave: the digit of the need-th largest candidate in a histogram of NB
+// bins (reg_bin layout), and how many of the candidates with that digit are
+// still needed.
+template <int NB>
+__device__ __forceinline__ void reg_pick_digit(const uint32_t *hist, uint32_t need,
+                                               TopkRegShared &sh) {
+  constexpr int per = NB / 64;
+  const int lane = threadIdx.x & 63;
+  uint32_t h[per];
+  const u32x4_t *src = reinterpret_cast<const u32x4_t *>(hist + reg_bin(per * lane));
+#pragma unroll
+  for (int i = 0; i < per / 4; ++i) {
+    const u32x4_t q = src[i];
+    h[4 * i] = q.x; h[4 * i + 1] = q.y; h[4 * i + 2] = q.z; h[4 * i + 3] = q.w;
+  }
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < per; ++i) mine += h[i];
+  const uint32_t suf = wave_suffix_sum(mine);
+  const uint32_t above = suf - mine;
+  if (above < need && suf >= need) {
+    uint32_t acc = above, digit = 0, rest = 0;
+    bool found = false;
+#pragma unroll
+    for (int i = per - 1; i >= 0; --i) {
+      const bool here = !found && acc + h[i] >= need;
+      digit = here ? (uint32_t)(per * lane + i) : digit;
+      rest = here ? need - acc : rest;
+      found |= here;
+      acc += h[i];
+    }
+    sh.digit = digit;
+    sh.need = rest;
+  }
+}
+
+template <int R>
+__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
+    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
+    int total_q, int max_seq_len, const float *__restrict__ scores, int64_t ld, int k,
+    int32_t *__restrict__ indices) {
+  __shared__ TopkRegShared sh;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row).t + 1;
+  int32_t *out = indices + (int64_t)row * k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float *src = scores + (int64_t)row * ld;
+  float v[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int i = u * kTopkThreads + tid;
+    v[u] = i < n ? src[i] : 0.0f;
+  }
+  for (int i = tid; i < 2 * kRegBinsWords; i += kTopkThreads) (&sh.hist[0][0])[i] = 0;
+  uint32_t key[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) key[u] = order_key(v[u]);
+  auto valid = [&](int u) { return u * kTopkThreads + tid < n; };
+  __syncthreads();
+
+  // pass 1: bits 31..21
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+    if (valid(u)) atomicAdd(&sh.hist[0][reg_bin(key[u] >> 21)], 1u);
+  __syncthreads();
+  if (wv == 0) reg_pick_digit<kBinsA>(sh.hist[0], (uint32_t)k, sh);
+  __syncthreads();
+  uint32_t prefix = sh.digit << 21, need = sh.need;
+  // pass 2: bits 20..10 of the keys matching the prefix; hist[0] is cleared
+  // for pass 3 meanwhile
+  for (int i = tid; i < kRegBinsWords; i += kTopkThreads) sh.hist[0][i] = 0;
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+    if (valid(u) && (key[u] >> 21) == (prefix >> 21))
+      atomicAdd(&sh.hist[1][reg_bin((key[u] >> 10) & 2047u)], 1u);
+  __syncthreads();
+  if (wv == 0) reg_pick_digit<kBinsA>(sh.hist[1], need, sh);
+  __syncthreads();
+  prefix |= sh.digit << 10;
+  need = sh.need;
+  // pass 3: bits 9..0
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+    if (valid(u) && (key[u] >> 10) == (prefix >> 10))
+      atomicAdd(&sh.hist[0][reg_bin(key[u] & 1023u)], 1u);
+  __syncthreads();
+  if (wv == 0) reg_pick_digit<kBinsA / 2>(sh.hist[0], need, sh);
+  __syncthreads();
+  const uint32_t tau = prefix | sh.digit;
+  need = sh.need;
+
+  // ordered emit
+  uint64_t mg[R], me[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    mg[u] = __ballot(valid(u) && key[u] > tau);
+    me[u] = __ballot(valid(u) && key[u] == tau);
+    if (lane == 0) sh.cnt[u * kTopkWaves + wv] = ((uint32_t)__popcll(mg[u]) << 16) |
+                                                 (uint32_t)__popcll(me[u]);
+  }
+  __syncthreads();
+  if (wv == 0) {
+    // exclusive scan of the R * 16 packed counts in (u, wave) order
+    constexpr int per = R * kTopkWaves / 64;
+    uint32_t c[per], tot = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) { c[i] = sh.cnt[per * lane + i]; tot += c[i]; }
+    uint32_t incl = tot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    uint32_t run = incl - tot;
+#pragma unroll
+    for (int i = 0; i < per; ++i) { sh.cnt[per * lane + i] = run; run += c[i]; }
+  }
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const uint32_t off = sh.cnt[u * kTopkWaves + wv];
+    const uint32_t gt_before = (off >> 16) + (uint32_t)__popcll(mg[u] & below);
+    const uint32_t eq_before = (off & 0xFFFFu) + (uint32_t)__popcll(me[u] & below);
+    const int pos = u * kTopkThreads + tid;
+    if ((mg[u] >> lane) & 1ull) {
+      out[gt_before + min(eq_before, need)] = pos;
+    } else if (((me[u] >> lane) & 1ull) && eq_before < need) {
+      out[gt_before + eq_before] = pos;
+    }
+  }
+}
+
 int chunks_of(int32_t max_seq_len) { return (max_seq_len + kChunk - 1) / kChunk; }
 
 bool two_phase(int32_t max_seq_len) { return max_seq_len > kChunk; }
@@ -338,6 +506,12 @@ bool topk_supported(int32_t max_seq_len, int32_t k) {
 hipError_t launch_topk(const BatchArgs &bt, const float *scores, int64_t ld, int32_t k,
                        int32_t *indices, void *workspace, size_t, hipStream_t stream) {
   if (bt.total_q == 0) return hipSuccess;
+  if (bt.max_seq_len <= 16 * kTopkThreads) {
+    auto kernel = bt.max_seq_len <= 8 * kTopkThreads ? topk_reg_kernel<8> : topk_reg_kernel<16>;
+    hipLaunchKernelGGL(kernel, dim3(bt.total_q), dim3(kTopkThreads), 0, stream, bt.seq_lens,
+                       bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, scores, ld, k, indices);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)kChunk * sizeof(uint32_t);
   hipError_t e;
   if (!two_phase(bt.max_seq_len)) {
