@@ -142,6 +142,215 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_mfma_kernel(
   }
 }
 
+// Streaming decode path (bf16 queries, bf16 or e4m3 keys, head_dim 128, pages
+// holding whole 64-key blocks). One 256-thread workgroup walks a run of
+// blocks of 64 consecutive keys of one sequence (16 blocks per query row of
+// the workgroup, fewer when the batch is small); each block is copied into an
+// LDS stage by direct global-to-LDS loads (16 bytes per lane, 1 KB per wave
+// instruction, the 16-byte chunks of each key XOR-permuted by the key's low
+// bits through the choice of source address) three blocks ahead of the one
+// being computed, with one barrier per block. Wave w multiplies the query
+// fragments held in registers with keys 16w..16w+15 of the block (operands
+// from LDS), so the memory system sees a few long contiguous streams per CU
+// instead of every key request of the launch at once.
+constexpr int kStreamBlocks = 16;  // blocks of scores buffered in LDS between write-outs
+constexpr int kStreamWorkgroups = 512;
+constexpr int kStreamStages = 4;
+constexpr int kStreamKeys = 64;
+
+// Direct global-to-LDS copy, 16 (or 4) bytes per lane, at lds + 16 l (4 l).
+// Issued as inline assembly so the compiler's automatic waits ignore it;
+// completion is awaited by the explicit vmcnt waits before the barriers.
+__device__ __forceinline__ void idx_lds_load16(const void *src, const __attribute__((address_space(3))) void *lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  uint32_t saved;  // m0 is reserved to the compiler: restore it
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(src), "s"(m0)
+               : "memory");
+}
+__device__ __forceinline__ void idx_lds_load4(const void *src, const __attribute__((address_space(3))) void *lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  uint32_t saved;  // m0 is reserved to the compiler: restore it
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(src), "s"(m0)
+               : "memory");
+}
+
+// s_waitcnt immediate: vmcnt n (bits 3:0, 15:14), expcnt and lgkmcnt 0.
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14); }
+
+// Workgroup barrier ordering LDS only: waits for this wave's LDS operations
+// (lgkmcnt 0) but not for memory loads in flight, which a full
+// __syncthreads() (release fence) would drain.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+template <int NMT, int QG, bool FP8>
+__global__ __launch_bounds__(256) void indexer_stream_kernel(
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ cu_q, int batch, int total_q, int max_seq_len, int64_t bt_stride,
+    const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
+    const uint8_t *__restrict__ kdata, const float *__restrict__ kscale, int64_t num_pages,
+    int page_size, FastDiv pdiv, float *__restrict__ scores, int64_t ld, int run_blocks) {
+  constexpr int H = NMT * 16;
+  constexpr int RB = FP8 ? kIdxDim : 2 * kIdxDim;    // bytes per key row
+  constexpr int CPK = RB / 16;                      // 16-byte chunks per key
+  constexpr int SB = kStreamKeys * RB;              // stage bytes
+  constexpr int NI = SB / 1024 / 4;                 // key copies per wave per block
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_st[kStreamStages][SB];
+  __shared__ __attribute__((aligned(256))) float s_sc[kStreamStages][kStreamKeys];
+  // scores of the workgroup's keys, written out after the loop so that the
+  // only memory operations inside it are the direct copies
+  __shared__ float s_out[QG][kStreamBlocks * kStreamKeys];
+
+  const int chunk = blockIdx.x, qgrp = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  if (b >= batch) return;
+  const int L = min(max(seq_lens[b], 0), max_seq_len);
+  const int q0 = min(max(cu_q[b], 0), total_q);
+  const int qn = min(max(cu_q[b + 1], q0), total_q) - q0;
+  const int i0 = qgrp * QG;
+  if (i0 >= qn) return;
+  const int nq = min(QG, qn - i0);
+  const int t_first = L - qn + i0;
+  const int t_last = t_first + nq - 1;
+  const int key0 = chunk * run_blocks * kStreamKeys;
+  if (t_last < 0 || key0 > t_last) return;
+  const int nblk = min(run_blocks, (t_last - key0) / kStreamKeys + 1);
+
+  // Query fragments: lane (g, j) holds head 16 mt + j, dims dim_of(s, g).
+  u32x4_t a[QG][NMT][4];
+  float wr[QG][NMT][4];
+#pragma unroll
+  for (int qi = 0; qi < QG; ++qi) {
+    const int64_t row = q0 + i0 + min(qi, nq - 1);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const uint16_t *qp = q_idx + (row * H + mt * 16 + j) * kIdxDim;
+#pragma unroll
+      for (int s_ = 0; s_ < 4; ++s_) a[qi][mt][s_] = ldg16(qp + dim_of<FP8>(s_, g));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wr[qi][mt][r] = w[row * H + mt * 16 + 4 * g + r];
+    }
+  }
+  // Copy map: wave wv's copy i of a block moves stage chunks 64 (4 i + wv) + l,
+  // i.e. key c / CPK, stored chunk c % CPK, fetched from chunk swz of the key.
+  auto swz = [](int c, int r) { return FP8 ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15)); };
+  uint32_t goff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int c = 64 * (4 * i + wv) + lane;
+    const int r = c / CPK, lc = c % CPK;
+    goff[i] = (uint32_t)(r * RB + 16 * swz(lc, r));
+  }
+  const int64_t bt_row = (int64_t)b * bt_stride;
+  auto copy_block = [&](int blk) {
+    const int kb0 = key0 + blk * kStreamKeys;
+    const int pidx = (int)fast_div((uint32_t)kb0, pdiv);
+    int64_t page = block_table[bt_row + pidx];
+    page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+    const int64_t row0 = page * page_size + (kb0 - pidx * page_size);
+    const uint8_t *base = kdata + row0 * RB;
+    const lds_u8 *st = (const lds_u8 *)s_st[blk % kStreamStages];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) idx_lds_load16(base + goff[i], st + 1024 * (4 * i + wv));
+    if constexpr (FP8) {
+      if (wv == 0) idx_lds_load4(kscale + row0 + lane, (const lds_u8 *)s_sc[blk % kStreamStages]);
+    }
+  };
+  // loads of this wave per block (the scale copy is wave 0's)
+  const int per_blk = NI + ((FP8 && wv == 0) ? 1 : 0);
+
+  // every compiler-visible load has landed before the first direct copies
+  __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+  for (int p = 0; p < kStreamStages - 1; ++p)
+    if (p < nblk) copy_block(p);
+
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int ahead = min(nblk - 1 - blk, kStreamStages - 2);
+    // this wave's copies of blk have landed
+    if (ahead >= 2) {
+      if (per_blk == NI) __builtin_amdgcn_s_waitcnt(vm_wait(2 * NI));
+      else __builtin_amdgcn_s_waitcnt(vm_wait(2 * NI + 2));
+    } else if (ahead == 1) {
+      if (per_blk == NI) __builtin_amdgcn_s_waitcnt(vm_wait(NI));
+      else __builtin_amdgcn_s_waitcnt(vm_wait(NI + 1));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    }
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (blk + kStreamStages - 1 < nblk) copy_block(blk + kStreamStages - 1);
+
+    const int tile0 = key0 + blk * kStreamKeys + 16 * wv;
+    if (tile0 <= t_last) {
+    const lds_u8 *st = (const lds_u8 *)s_st[blk % kStreamStages];
+    const int kr = 16 * wv + j;  // key of this lane within the block
+    u32x4_t bb[4];
+    if constexpr (FP8) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4_t src = *(const __attribute__((address_space(3))) u32x4_t *)(
+            st + kr * RB + 16 * swz(2 * g + h, kr));
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const u32x2_t lo = e4m3x4_to_bf16x4(e ? src.z : src.x);
+          const u32x2_t hi = e4m3x4_to_bf16x4(e ? src.w : src.y);
+          bb[2 * h + e] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s_ = 0; s_ < 4; ++s_)
+        bb[s_] = *(const __attribute__((address_space(3))) u32x4_t *)(st + kr * RB + 16 * swz(4 * s_ + g, kr));
+    }
+    const float ksc = FP8 ? *(const __attribute__((address_space(3))) float *)((const lds_u8 *)s_sc[blk % kStreamStages] + 4 * kr) : 1.0f;
+    const int pos = tile0 + j;
+#pragma unroll
+    for (int qi = 0; qi < QG; ++qi) {
+      float p = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s_ = 0; s_ < 4; ++s_) acc = mfma_16x16x32_bf16(a[qi][mt][s_], bb[s_], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p = fmaf(wr[qi][mt][r], relu_bits(acc[r]), p);
+      }
+      // head sum over the four lane groups; the positive per-key scale of
+      // e4m3 keys factors out of the ReLU
+      auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+      p = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+      auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+      p = (__uint_as_float(s32[0]) + __uint_as_float(s32[1])) * ksc;
+      if ((qi & 3) == g) s_out[qi][(blk % kStreamBlocks) * kStreamKeys + 16 * wv + j] = p;
+    }
+    }
+    // every kStreamBlocks blocks (and at the end) write the buffered scores out
+    if (blk % kStreamBlocks == kStreamBlocks - 1 || blk == nblk - 1) {
+      lds_barrier();
+      const int base = key0 + (blk - blk % kStreamBlocks) * kStreamKeys;  // first buffered key
+      const int nbuf = (blk % kStreamBlocks + 1) * kStreamKeys;
+#pragma unroll
+      for (int qi = 0; qi < QG; ++qi) {
+        if (qi >= nq) break;
+        const int lim = min(nbuf, t_first + qi + 1 - base);  // causal: pos <= t
+        float *dst = scores + (int64_t)(q0 + i0 + qi) * ld + base;
+        for (int i = tid; i < lim; i += 256) dst[i] = s_out[qi][i];
+      }
+      lds_barrier();
+    }
+  }
+}
+
 // Prefill path (bf16 queries and keys, head_dim 128, many queries per
 // sequence). The scores of a block of consecutive query rows form a GEMM
 // [rows x heads, 128] x [128, keys] followed by the per-head ReLU and weighted
@@ -455,9 +664,48 @@ hipError_t launch_prefill(const BatchArgs &bt, const void *q_idx, const float *w
   return hipGetLastError();
 }
 
+template <int NMT, int QG, bool FP8>
+hipError_t launch_stream(const BatchArgs &bt, const void *q_idx, const float *w,
+                         const CacheArgs &keys, float *scores, int64_t ld, hipStream_t stream) {
+  const int qgroups = (bt.max_q + QG - 1) / QG;
+  const int64_t seq_blocks = (bt.max_seq_len + kStreamKeys - 1) / kStreamKeys;
+  const int64_t units = (int64_t)qgroups * bt.batch;
+  // kStreamBlocks blocks per query row of the group (the query block a
+  // workgroup loads grows with the group; short runs keep ragged batches
+  // balanced), shortened when the batch would give too few workgroups
+  int64_t run = (int64_t)kStreamBlocks * QG;
+  run = std::min<int64_t>(run, std::max<int64_t>(kStreamBlocks,
+                                                 seq_blocks * units / kStreamWorkgroups));
+  run = std::min<int64_t>(run, seq_blocks);
+  const int64_t chunks = (seq_blocks + run - 1) / run;
+  if (qgroups > 65535 || bt.batch > 65535 || chunks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)chunks, qgroups, bt.batch);
+  hipLaunchKernelGGL((indexer_stream_kernel<NMT, QG, FP8>), grid, dim3(256), 0, stream,
+                     bt.block_table, bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len,
+                     bt.bt_stride, static_cast<const uint16_t *>(q_idx), w,
+                     static_cast<const uint8_t *>(keys.data), keys.scale, keys.num_pages,
+                     keys.page_size, make_fast_div((uint32_t)keys.page_size), scores, ld, (int)run);
+  return hipGetLastError();
+}
+
 template <bool FP8>
 hipError_t dispatch_mfma(const BatchArgs &bt, const void *q_idx, const float *w, int n_heads,
                          const CacheArgs &keys, float *scores, int64_t ld, hipStream_t stream) {
+  // pages holding whole 64-key blocks: stream the keys through LDS
+  if (keys.page_size % kStreamKeys == 0 && bt.max_q < kPrefillMinQ) {
+    const bool multi = bt.max_q > 1;
+    switch (n_heads) {
+      case 16:
+        return multi ? launch_stream<1, 4, FP8>(bt, q_idx, w, keys, scores, ld, stream)
+                     : launch_stream<1, 1, FP8>(bt, q_idx, w, keys, scores, ld, stream);
+      case 32:
+        return multi ? launch_stream<2, 4, FP8>(bt, q_idx, w, keys, scores, ld, stream)
+                     : launch_stream<2, 1, FP8>(bt, q_idx, w, keys, scores, ld, stream);
+      default:
+        return multi ? launch_stream<4, 2, FP8>(bt, q_idx, w, keys, scores, ld, stream)
+                     : launch_stream<4, 1, FP8>(bt, q_idx, w, keys, scores, ld, stream);
+    }
+  }
   if (!FP8 && bt.max_q >= kPrefillMinQ) {
     switch (n_heads) {
       case 16: return launch_prefill<16>(bt, q_idx, w, keys, scores, ld, stream);

@@ -103,8 +103,11 @@ __device__ __forceinline__ uint2 lds_read_tr16(const __attribute__((address_spac
 // every tile on the copies three tiles ahead).
 __device__ __forceinline__ void lds_load16(const void *src, const __attribute__((address_space(3))) void *lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
-               : "memory", "m0");
+  uint32_t saved;  // m0 is reserved to the compiler: restore it
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(src), "s"(m0)
+               : "memory");
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
