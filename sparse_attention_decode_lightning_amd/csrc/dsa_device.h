@@ -118,39 +118,46 @@ __device__ __forceinline__ float relu_bits(float x) {
   return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
 }
 
-// Sequence of a flattened query row: the largest b < batch with
-// cu_q[b] <= row (0 if none). Wave-cooperative: every lane of the wave must be
-// active and pass the same row. Each lane tests one offset per 64-sequence
-// chunk; with non-decreasing offsets the hits form a prefix, so one load per
-// lane and a ballot replace a chain of dependent loads.
-__device__ __forceinline__ int find_seq(const int32_t *cu_q, int batch, int row) {
-  const int lane = threadIdx.x & 63;
-  int b = 0;
-  for (int base = 0; base < batch; base += 64) {
-    const int i = base + lane;
-    const uint64_t hit = __ballot(i < batch && cu_q[i] <= row);
-    if (hit != 0ull) b = base + 63 - __clzll(hit);
-    if (hit != ~0ull) break;
-  }
-  return b;
-}
-
 struct RowInfo {
   int b;  // sequence of the row
   int t;  // absolute position of the row; -1 if the metadata leaves it none
 };
 
-// Sequence and causal position of a flattened query row (wave-cooperative,
-// as find_seq), with every value
+// Sequence and causal position of a flattened query row: b is the largest
+// b < batch with cu_q[b] <= row (0 if none). Wave-cooperative: every lane of
+// the wave must be active and pass the same row. With non-decreasing offsets
+// the lanes whose offset is <= row form a prefix, so one load per lane and a
+// ballot replace a chain of dependent loads. Every value is
 // clamped so malformed metadata can never index past the caller's buffers:
 // q offsets into [0, total_q], lengths into [0, max_seq_len], t <= L - 1.
+// One round trip: with the offset each lane also loads the next offset and
+// the length of its sequence, and the row's three values are read from the
+// lane of the sequence found (lane 0 of the first chunk when none is).
 __device__ __forceinline__ RowInfo row_info(const int32_t *cu_q, const int32_t *seq_lens,
                                             int batch, int total_q, int max_seq_len, int row) {
+  const int lane = threadIdx.x & 63;
+  int b = 0, c0 = 0, c1 = 0, len = 0;
+  for (int base = 0; base < batch; base += 64) {
+    const int i = base + lane;
+    const bool in = i < batch;
+    const int a0 = in ? cu_q[i] : 0;
+    const int a1 = in ? cu_q[i + 1] : 0;
+    const int al = in ? seq_lens[i] : 0;
+    const uint64_t hit = __ballot(in && a0 <= row);
+    if (base == 0 || hit != 0ull) {
+      const int src = hit != 0ull ? 63 - __clzll(hit) : 0;
+      b = base + src;
+      c0 = __builtin_amdgcn_readlane(a0, src);
+      c1 = __builtin_amdgcn_readlane(a1, src);
+      len = __builtin_amdgcn_readlane(al, src);
+    }
+    if (hit != ~0ull) break;
+  }
   RowInfo ri;
-  ri.b = find_seq(cu_q, batch, row);
-  const int q0 = min(max(cu_q[ri.b], 0), total_q);
-  const int q1 = min(max(cu_q[ri.b + 1], q0), total_q);
-  const int L = min(max(seq_lens[ri.b], 0), max_seq_len);
+  ri.b = b;
+  const int q0 = min(max(c0, 0), total_q);
+  const int q1 = min(max(c1, q0), total_q);
+  const int L = min(max(len, 0), max_seq_len);
   const int t = L - (q1 - q0) + (row - q0);
   ri.t = (row < q0 || row >= q1) ? -1 : min(t, L - 1);
   ri.t = ri.t < -1 ? -1 : ri.t;

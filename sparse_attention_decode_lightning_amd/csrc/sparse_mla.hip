@@ -95,19 +95,70 @@ __device__ __forceinline__ uint2 lds_read_tr16(const __attribute__((address_spac
   return __builtin_bit_cast(uint2, v);
 }
 
-// Direct global-to-LDS copy of 16 bytes per lane: lane l's bytes land at
-// lds + 16 l (lds wave-uniform). Issued as inline assembly so the compiler's
-// automatic waits ignore it: its completion is awaited only by the explicit
-// vmcnt waits before the tile barriers (the compiler's per-buffer tracking of
-// such copies does not survive the tile loop's back edge, and would stall
-// every tile on the copies three tiles ahead).
-__device__ __forceinline__ void lds_load16(const void *src, const __attribute__((address_space(3))) void *lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  uint32_t saved;  // m0 is reserved to the compiler: restore it
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved)
-               : "v"(src), "s"(m0)
-               : "memory");
+// Direct global-to-LDS copy of one wave's eight rows of a tile: nine 16-byte
+// loads per lane, instruction n landing at lds + 1024 n + 16 lane (lds
+// wave-uniform). The loads go out in groups of four sharing one m0 value
+// (lds, lds + 4096, lds + 8192); the rest of the 1024 n step comes from the
+// instruction offset, which moves the LDS and the global address alike, so
+// the caller's address for instruction n is 1024 (n % 4) below its source.
+// Issued as inline assembly so the compiler's automatic waits ignore the
+// copies: their completion is awaited only by the explicit vmcnt waits before
+// the tile barriers (the compiler's per-buffer tracking of such copies does
+// not survive the tile loop's back edge, and would stall every tile on the
+// copies three tiles ahead). m0 is reserved to the compiler and restored; one
+// wait state separates each m0 write from the copies that read it.
+// Addresses as 32-bit offsets from a scalar base (pools below 4 GiB) ...
+__device__ __forceinline__ void lds_copy9(const uint8_t *base, const uint32_t (&v)[9], uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %10\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %11\n\t"
+      "global_load_lds_dwordx4 %2, %11 offset:1024\n\t"
+      "global_load_lds_dwordx4 %3, %11 offset:2048\n\t"
+      "global_load_lds_dwordx4 %4, %11 offset:3072\n\t"
+      "s_add_u32 m0, %10, 0x1000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %5, %11\n\t"
+      "global_load_lds_dwordx4 %6, %11 offset:1024\n\t"
+      "global_load_lds_dwordx4 %7, %11 offset:2048\n\t"
+      "global_load_lds_dwordx4 %8, %11 offset:3072\n\t"
+      "s_add_u32 m0, %10, 0x2000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %9, %11\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]),
+        "v"(v[8]), "s"(lds), "s"(base)
+      : "memory", "scc");
+}
+
+// ... or as full 64-bit addresses (any pool size).
+__device__ __forceinline__ void lds_copy9(const uint64_t (&v)[9], uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %10\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %2, off offset:1024\n\t"
+      "global_load_lds_dwordx4 %3, off offset:2048\n\t"
+      "global_load_lds_dwordx4 %4, off offset:3072\n\t"
+      "s_add_u32 m0, %10, 0x1000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %5, off\n\t"
+      "global_load_lds_dwordx4 %6, off offset:1024\n\t"
+      "global_load_lds_dwordx4 %7, off offset:2048\n\t"
+      "global_load_lds_dwordx4 %8, off offset:3072\n\t"
+      "s_add_u32 m0, %10, 0x2000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %9, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]),
+        "v"(v[8]), "s"(lds)
+      : "memory", "scc");
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -129,19 +180,16 @@ __device__ __forceinline__ float group4_sum(float v) {
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+template <bool kOff32>
 __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ cu_q, int batch, int total_q, int max_seq_len, int64_t bt_stride,
     const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv, int64_t num_pages,
-    int page_size, const int32_t *__restrict__ indices, int k, int n_splits, int rows_per_split,
-    float scale_log2, float *__restrict__ out, float *__restrict__ lse,
+    int page_size, FastDiv pdiv, const int32_t *__restrict__ indices, int k, int n_splits,
+    int rows_per_split, float scale_log2, float *__restrict__ out, float *__restrict__ lse,
     float *__restrict__ ws_acc, float *__restrict__ ws_ml) {
-  // four separate stage arrays (not one indexed array), so that reads of one
-  // stage are not ordered behind the direct loads still landing in the others
-  __shared__ __attribute__((aligned(1024))) uint8_t s_st0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_st1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_st2[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_st3[kTileBytes];
+  // ring of row tiles: tile i lives in stage i % kStages
+  __shared__ __attribute__((aligned(1024))) uint8_t s_tiles[kStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) uint32_t s_rowid[kMaxRowsPerSplit + kTileN];
   __shared__ uint32_t s_vmask[kMaxRowsPerSplit / kTileN + 1];
   __shared__ float s_ml[kH][2];
@@ -157,19 +205,15 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, j = lane & 15;
 
-  const RowInfo ri = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row);
-  const int b = ri.b, t = ri.t;
   const int slot_begin = split * rows_per_split;
   const int slot_end = min(k, slot_begin + rows_per_split);
   const int nrows = max(0, slot_end - slot_begin);
   const int ntiles = (nrows + kTileN - 1) / kTileN;
-  const int32_t *idx_row = indices + (int64_t)row * k;
-  // A valid row to load in place of masked slots (position 0 of the sequence).
-  const uint32_t safe_row =
-      t >= 0 ? (uint32_t)paged_row(block_table, bt_stride, b, 0, page_size, num_pages) : 0u;
+  const int32_t *idx_row = indices + (int64_t)row * k + slot_begin;
 
-  // Query block of heads 16wv..16wv+15, the B operand of the logits: lane
-  // (g, j) holds head 16wv + j, dims 32s + 8g .. +8.
+  // The query block of heads 16wv..16wv+15, the B operand of the logits:
+  // lane (g, j) holds head 16wv + j, dims 32s + 8g .. +8. Issued first: it
+  // lands while the row table's two dependent round trips below are in flight.
   u32x4_t qf[kSteps];
   {
     const uint16_t *qp = q + ((int64_t)row * kH + 16 * wv + j) * kD + 8 * g;
@@ -177,18 +221,48 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     for (int s = 0; s < kSteps; ++s) qf[s] = ldg16(qp + 32 * s);
   }
 
-  // Row table: physical row of every slot of the split, masked slots flagged.
-  for (int base = 0; base < ntiles * kTileN; base += kMlaThreads) {
-    const int i = base + tid;
-    bool valid = false;
-    uint32_t rid = safe_row;
-    if (i < nrows) {
-      const int pos = idx_row[slot_begin + i];
-      if (pos >= 0 && pos <= t) {
-        valid = true;
-        rid = (uint32_t)paged_row(block_table, bt_stride, b, pos, page_size, num_pages);
-      }
+  // Row table, first round trip: the selected positions of this thread's
+  // entries (entry e covers slot kMlaThreads e + tid of the split), and in
+  // parallel the row's sequence and causal position.
+  constexpr int kEntries = kMaxRowsPerSplit / kMlaThreads;
+  int pos[kEntries];
+#pragma unroll
+  for (int e = 0; e < kEntries; ++e) {
+    const int i = e * kMlaThreads + tid;
+    pos[e] = i < nrows ? idx_row[i] : -1;
+  }
+  const RowInfo ri = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row);
+  const int b = ri.b, t = ri.t;
+
+  // Second round trip: the page of every entry (positions clamped into
+  // [0, t] so the reads stay inside the row's table whatever a slot holds;
+  // slots outside it are masked below) and the page of position 0 (the
+  // stand-in row of masked slots).
+  int page[kEntries];
+  int page0 = 0;
+  if (t >= 0) {
+    const int32_t *bt_row = block_table + (int64_t)b * bt_stride;
+#pragma unroll
+    for (int e = 0; e < kEntries; ++e) {
+      const int p = min(max(pos[e], 0), t);
+      page[e] = e * kMlaThreads + tid < ntiles * kTileN ? bt_row[fast_div((uint32_t)p, pdiv)] : 0;
     }
+    page0 = bt_row[0];
+  }
+  auto clamp_page = [&](int64_t pg) -> uint32_t {
+    return (uint32_t)(pg < 0 ? 0 : (pg >= num_pages ? num_pages - 1 : pg));
+  };
+  const uint32_t safe_row = clamp_page(page0) * (uint32_t)page_size;
+#pragma unroll
+  for (int e = 0; e < kEntries; ++e) {
+    const int i = e * kMlaThreads + tid;
+    if (e * kMlaThreads >= ntiles * kTileN) break;
+    const int p = pos[e];
+    const bool valid = i < nrows && p >= 0 && p <= t;
+    const uint32_t pq = fast_div((uint32_t)max(p, 0), pdiv);
+    const uint32_t rid =
+        valid ? clamp_page(page[e]) * (uint32_t)page_size + ((uint32_t)p - pq * (uint32_t)page_size)
+              : safe_row;
     if (i < ntiles * kTileN) s_rowid[i] = valid ? rid : (rid | kInvalid);
     const uint64_t vb = __ballot(valid && i < ntiles * kTileN);
     if (lane == 0 && i < ntiles * kTileN) {
@@ -198,48 +272,52 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
   }
 
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
-  auto stage = [&](auto st) -> lds_u8 * {
-    constexpr int ST = decltype(st)::value;
-    if constexpr (ST == 0) return (lds_u8 *)s_st0;
-    else if constexpr (ST == 1) return (lds_u8 *)s_st1;
-    else if constexpr (ST == 2) return (lds_u8 *)s_st2;
-    else return (lds_u8 *)s_st3;
-  };
+  const lds_u8 *tiles = (const lds_u8 *)s_tiles;
+  const uint32_t lds_tiles = (uint32_t)(uintptr_t)tiles;
   // Gather map: instruction n of wave wv moves chunks 64n..64n+63 of the 576
   // chunks of rows 8wv..8wv+7; lane l's chunk is row 8wv + (64n+l)/72, stored
   // chunk (64n+l)%72, fetched from that row's chunk chunk_swz(., row). The
   // row is one of two known to the instruction: 64n/72, or the next from lane
-  // 72(64n/72 + 1) - 64n on.
+  // 72(64n/72 + 1) - 64n on. goff[n] holds the chunk's byte offset in its
+  // row, less the 1024 (n % 4) that the copy's instruction offset adds back
+  // (plus 3072 on the 32-bit path, whose base sits 3072 bytes below the cache
+  // so that every offset stays non-negative).
+  constexpr uint32_t kBias = kOff32 ? 3072u : 0u;
   uint32_t goff[kGatherInsts];
 #pragma unroll
   for (int n = 0; n < kGatherInsts; ++n) {
     const int qc = 64 * n + lane;
     const int rl = qc / 72, lc = qc % 72;
-    goff[n] = (uint32_t)(16 * chunk_swz(lc, 8 * wv + rl));
+    goff[n] = (uint32_t)(16 * chunk_swz(lc, 8 * wv + rl)) + kBias - 1024u * (n % 4);
   }
-  auto gather = [&](auto st, int tile) {
-    lds_u8 *dst = stage(st) + 8 * wv * kRowBytes;
+  const uint8_t *kv_base = kv - kBias;
+  auto gather = [&](int tile) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        lds_tiles + (uint32_t)(tile & (kStages - 1)) * kTileBytes + 8 * wv * kRowBytes);
     const u32x4_t ra = *reinterpret_cast<const u32x4_t *>(s_rowid + tile * kTileN + 8 * wv);
     const u32x4_t rb = *reinterpret_cast<const u32x4_t *>(s_rowid + tile * kTileN + 8 * wv + 4);
-    uint32_t rid[9];
-    rid[0] = __builtin_amdgcn_readfirstlane(ra.x) & ~kInvalid;
-    rid[1] = __builtin_amdgcn_readfirstlane(ra.y) & ~kInvalid;
-    rid[2] = __builtin_amdgcn_readfirstlane(ra.z) & ~kInvalid;
-    rid[3] = __builtin_amdgcn_readfirstlane(ra.w) & ~kInvalid;
-    rid[4] = __builtin_amdgcn_readfirstlane(rb.x) & ~kInvalid;
-    rid[5] = __builtin_amdgcn_readfirstlane(rb.y) & ~kInvalid;
-    rid[6] = __builtin_amdgcn_readfirstlane(rb.z) & ~kInvalid;
-    rid[7] = __builtin_amdgcn_readfirstlane(rb.w) & ~kInvalid;
-    rid[8] = rid[7];
+    const uint32_t rid[8] = {ra.x & ~kInvalid, ra.y & ~kInvalid, ra.z & ~kInvalid, ra.w & ~kInvalid,
+                             rb.x & ~kInvalid, rb.y & ~kInvalid, rb.z & ~kInvalid, rb.w & ~kInvalid};
+    if constexpr (kOff32) {
+      uint32_t v[kGatherInsts];
 #pragma unroll
-    for (int n = 0; n < kGatherInsts; ++n) {
-      constexpr int kq[kGatherInsts] = {0, 0, 1, 2, 3, 4, 5, 6, 7};
-      const int q0 = (64 * n) / 72;
-      const int split_lane = 72 * (q0 + 1) - 64 * n;
-      const uint32_t r = lane < split_lane ? rid[q0] : rid[q0 + 1];
-      (void)kq;
-      const uint8_t *src = kv + (int64_t)r * kRowBytes + goff[n];
-      lds_load16(src, dst + 1024 * n);
+      for (int n = 0; n < kGatherInsts; ++n) {
+        const int q0 = (64 * n) / 72;
+        const int split_lane = 72 * (q0 + 1) - 64 * n;
+        const uint32_t r = (q0 == 7 || lane < split_lane) ? rid[q0] : rid[q0 + 1];
+        v[n] = __umul24(r, (uint32_t)kRowBytes) + goff[n];
+      }
+      lds_copy9(kv_base, v, lds);
+    } else {
+      uint64_t v[kGatherInsts];
+#pragma unroll
+      for (int n = 0; n < kGatherInsts; ++n) {
+        const int q0 = (64 * n) / 72;
+        const int split_lane = 72 * (q0 + 1) - 64 * n;
+        const uint32_t r = (q0 == 7 || lane < split_lane) ? rid[q0] : rid[q0 + 1];
+        v[n] = (uint64_t)((int64_t)(uintptr_t)kv + (int64_t)r * kRowBytes + (int32_t)goff[n]);
+      }
+      lds_copy9(v, lds);
     }
   };
 
@@ -280,8 +358,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
   __builtin_amdgcn_s_waitcnt(0x0070);
   __syncthreads();  // row table visible
 
-  auto step = [&](auto st, int tile) -> bool {
-    constexpr int ST = decltype(st)::value;
+  auto step = [&](int tile) {
     // this wave's loads of `tile` have landed (later tiles may be in flight)
     const int ahead = min(ntiles - 1 - tile, kStages - 2);
     // (s_waitcnt fields: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8;
@@ -295,12 +372,12 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     // every wave is done with the stage of tile - 1.
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if ((s_over[0] | s_over[1] | s_over[2] | s_over[3]) != 0) return true;  // an earlier tile overflowed
-    if (tile + kStages - 1 < ntiles) gather(std::integral_constant<int, (ST + kStages - 1) % kStages>{}, tile + kStages - 1);
+    if (tile + kStages - 1 < ntiles) gather(tile + kStages - 1);
 
+    // (a fully masked tile is computed like any other: its logits are all
+    // -inf and add nothing)
     const uint32_t vmask = s_vmask[tile];
-    if (vmask == 0u) return false;
-    const lds_u8 *tb = stage(st);
+    const lds_u8 *tb = tiles + (tile & (kStages - 1)) * kTileBytes;
 
     // logits (transposed): acc[m][r] = S[head 16wv + j][row lrow[m][r]], A
     // operands read one k-step ahead of the MFMAs
@@ -358,12 +435,14 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     // the flag is read by all waves after the next barrier (a restarted
     // split discards whatever this tile accumulates)
     s_over[wv] = __ballot(overflow) != 0ull ? 1 : 0;
+    // until the head's first valid row every logit is -inf: subtract 0, not -inf
+    const float m_sub = m_run == -INFINITY ? 0.0f : m_run;
     float p[2][4];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[m][r] = fast_exp2(fmaf(acc[m][r], scale_log2, -m_run));
+        p[m][r] = fast_exp2(fmaf(acc[m][r], scale_log2, -m_sub));
         l_run += p[m][r];
       }
     // P as the A operand of PV: head j, k-slots 8g + 4m + r <-> rows lrow[m][r].
@@ -408,23 +487,17 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * kVAhead, 0);
-    return false;
   };
 
-  // Passes over the split: normally one. A pass that meets an overflowing
-  // tile is abandoned by every wave at the next barrier (the flag is read
-  // after it), its loads are drained, and the split is walked again.
+  // Passes over the split: normally one. A pass in which some tile
+  // overflowed runs to its end (its sums stay finite: the reference is raised
+  // before the overflowing tile's probabilities are taken, and every earlier
+  // one is at most 2^kHeadroom), then the split is walked again from the
+  // raised references. Not leaving the tile loop early keeps the
+  // accumulators in the registers the MFMAs write.
   for (;;) {
-    if (0 < ntiles) gather(std::integral_constant<int, 0>{}, 0);
-    if (1 < ntiles) gather(std::integral_constant<int, 1>{}, 1);
-    if (2 < ntiles) gather(std::integral_constant<int, 2>{}, 2);
-    bool restart = false;
-    for (int tile = 0; tile < ntiles && !restart; tile += kStages) {
-      restart = step(std::integral_constant<int, 0>{}, tile);
-      if (!restart && tile + 1 < ntiles) restart = step(std::integral_constant<int, 1>{}, tile + 1);
-      if (!restart && tile + 2 < ntiles) restart = step(std::integral_constant<int, 2>{}, tile + 2);
-      if (!restart && tile + 3 < ntiles) restart = step(std::integral_constant<int, 3>{}, tile + 3);
-    }
+    for (int tile = 0; tile < min(ntiles, kStages - 1); ++tile) gather(tile);
+    for (int tile = 0; tile < ntiles; ++tile) step(tile);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no direct load of this pass in flight
     __syncthreads();
     if ((s_over[0] | s_over[1] | s_over[2] | s_over[3]) == 0) break;
@@ -477,26 +550,49 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
 
 // Merge the splits of one row: 256 threads = 4 heads x 64 threads x 8 dims.
 // O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, lse = M ln 2 + ln(sum ...).
+// Splits are taken eight at a time with every load of the eight issued before
+// any is used.
 __global__ __launch_bounds__(256) void mla_combine_kernel(int n_splits,
                                                           const float *__restrict__ ws_acc,
                                                           const float *__restrict__ ws_ml,
                                                           float *__restrict__ out,
                                                           float *__restrict__ lse) {
+  constexpr int kU = 8;
   const int row = blockIdx.x / (kH / 4);
   const int head = (blockIdx.x % (kH / 4)) * 4 + (threadIdx.x >> 6);
   const int d0 = (threadIdx.x & 63) * 8;
   const float *ml = ws_ml + ((int64_t)row * n_splits * kH + head) * 2;  // split s at + s*kH*2
+  const float *acc = ws_acc + (((int64_t)row * n_splits * kH + head) * kDL + d0);  // + s*kH*kDL
   float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, ml[s * kH * 2]);
+  for (int s0 = 0; s0 < n_splits; s0 += kU) {
+    float m[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) m[u] = s0 + u < n_splits ? ml[(s0 + u) * kH * 2] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) M = fmaxf(M, m[u]);
+  }
   const float Mu = M == -INFINITY ? 0.0f : M;
   float Lsum = 0.0f;
   f32x4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int s = 0; s < n_splits; ++s) {
-    const float wgt = exp2f(ml[s * kH * 2] - Mu);
-    Lsum += wgt * ml[s * kH * 2 + 1];
-    const float *src = ws_acc + ((((int64_t)row * n_splits + s) * kH + head) * kDL + d0);
-    a0 += wgt * *reinterpret_cast<const f32x4_t *>(src);
-    a1 += wgt * *reinterpret_cast<const f32x4_t *>(src + 4);
+  for (int s0 = 0; s0 < n_splits; s0 += kU) {
+    float m[kU], l[kU];
+    f32x4_t x0[kU], x1[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool in = s0 + u < n_splits;
+      const float *src = acc + (int64_t)(s0 + u) * kH * kDL;
+      m[u] = in ? ml[(s0 + u) * kH * 2] : -INFINITY;
+      l[u] = in ? ml[(s0 + u) * kH * 2 + 1] : 0.0f;
+      x0[u] = in ? *reinterpret_cast<const f32x4_t *>(src) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      x1[u] = in ? *reinterpret_cast<const f32x4_t *>(src + 4) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float wgt = exp2f(m[u] - Mu);
+      Lsum += wgt * l[u];
+      a0 += wgt * x0[u];
+      a1 += wgt * x1[u];
+    }
   }
   const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
   float *dst = out + (((int64_t)row * kH + head) * kDL + d0);
@@ -603,12 +699,17 @@ hipError_t launch_sparse_mla(const BatchArgs &bt, const void *q, int32_t q_dtype
     float *ws_ml = ws_acc == nullptr ? nullptr
                                      : ws_acc + (size_t)bt.total_q * S * n_heads * d_latent;
     const int64_t rows_padded = (int64_t)(bt.total_q + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL(sparse_mla_bf16_kernel, dim3((unsigned)(rows_padded * S)),
-                       dim3(kMlaThreads), 0, stream, bt.block_table, bt.seq_lens, bt.cu_q,
-                       bt.batch, bt.total_q, bt.max_seq_len, bt.bt_stride,
-                       static_cast<const uint16_t *>(q), static_cast<const uint8_t *>(kv.data),
-                       kv.num_pages, kv.page_size, indices, k, S, per, scale_log2, out, lse,
-                       ws_acc, ws_ml);
+    // 32-bit row offsets (from a base 3072 bytes below the cache) when the
+    // whole pool lies within 4 GiB of that base
+    const uint64_t pool_bytes = (uint64_t)kv.num_pages * (uint64_t)kv.page_size * kRowBytes;
+    auto kern = pool_bytes + 4096 <= (1ull << 32) ? sparse_mla_bf16_kernel<true>
+                                                    : sparse_mla_bf16_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(rows_padded * S)), dim3(kMlaThreads), 0, stream,
+                       bt.block_table, bt.seq_lens, bt.cu_q, bt.batch, bt.total_q,
+                       bt.max_seq_len, bt.bt_stride, static_cast<const uint16_t *>(q),
+                       static_cast<const uint8_t *>(kv.data), kv.num_pages, kv.page_size,
+                       make_fast_div((uint32_t)kv.page_size), indices, k, S, per, scale_log2, out,
+                       lse, ws_acc, ws_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     hipLaunchKernelGGL(mla_combine_kernel, dim3(bt.total_q * (n_heads / 4)), dim3(256), 0, stream,
