@@ -37,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, vendor figure (no sparsity)
 WORKLOAD_DEFAULT = "decode_b32_l8k"
 
 
@@ -51,6 +52,14 @@ def parse():
                     help="replay the step as a captured HIP graph instead of eager launches")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed steps, copy 256 MiB device to device once (the "
+                         "reference for scaling rocprofv3 byte counters)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn two rocprofv3 --pmc runs of this script "
+                         "(FETCH_SIZE, WRITE_SIZE) into profiles/traffic_<workload>.json")
+    ap.add_argument("--commands", nargs="*", default=[],
+                    help="with --traffic-summary: the commands that made the runs")
     return ap.parse_args()
 
 
@@ -129,16 +138,91 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def committed_traffic(workload: str, kernel: str):
-    """Per-launch HBM bytes measured with rocprofv3 counters, if taken on the current sources."""
+# Kernels behind each library call (substrings of the kernel symbols); a call's
+# traffic is the sum over its kernels per call.
+STAGE_KERNELS = {
+    "indexer": ["indexer_"],
+    "topk": ["topk_"],
+    "sparse_mla": ["sparse_mla_", "mla_combine_kernel"],
+}
+COPY_PROBE_BYTES = 256 << 20
+
+
+def committed_traffic(workload: str, stage: str):
+    """HBM bytes per call of a stage, from rocprofv3 FETCH_SIZE/WRITE_SIZE counters taken on
+    the current kernel sources and scaled by a plain copy of known size; None otherwise."""
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
     if d.get("source_hash") != kernel_source_hash():
         return None
-    k = d.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
+    st = d.get("stages", {}).get(stage)
+    return None if st is None else st.get("bytes_per_call")
+
+
+def _pmc_rows(run_dir: str, counter: str):
+    """(kernel name, value in bytes) per dispatch from a rocprofv3 --pmc csv run directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for r in csv.DictReader(open(files[0])):
+        if r.get("Counter_Name") != counter:
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        name = r["Kernel_Name"]
+        per.setdefault(key, [name, 0.0])[1] += float(r["Counter_Value"]) * 1024.0  # KiB
+    return list(per.values())
+
+
+def traffic_summary(fetch_dir: str, write_dir: str, workload: str, calls_per_stage: dict,
+                    commands: list):
+    """Write profiles/traffic_<workload>.json from two counter runs of
+    `bench.py --copy-probe` (one FETCH_SIZE, one WRITE_SIZE)."""
+    fetch, write = _pmc_rows(fetch_dir, "FETCH_SIZE"), _pmc_rows(write_dir, "WRITE_SIZE")
+
+    def probe(rows):  # the largest plain copy is the probe
+        copies = [v for n, v in rows if "copyBuffer" in n or "copy" in n.lower()]
+        return max(copies) if copies else None
+
+    pf, pw = probe(fetch), probe(write)
+    f_scale = COPY_PROBE_BYTES / pf if pf else 1.0
+    w_scale = COPY_PROBE_BYTES / pw if pw else 1.0
+    kernels = {}
+    for rows, field, scale in ((fetch, "fetch", f_scale), (write, "write", w_scale)):
+        for name, v in rows:
+            if not any(sub in name for subs in STAGE_KERNELS.values() for sub in subs):
+                continue
+            short = name.replace("void ", "").replace("(anonymous namespace)::", "")
+            short = short.split("(")[0].split("::")[-1]
+            k = kernels.setdefault(short, {"fetch": [], "write": []})
+            k[field].append(v * scale)
+    out_k = {}
+    for short, k in kernels.items():
+        f = float(np.median(k["fetch"])) if k["fetch"] else 0.0
+        w = float(np.median(k["write"])) if k["write"] else 0.0
+        out_k[short] = {"fetch_bytes_per_launch": f, "write_bytes_per_launch": w,
+                        "bytes_per_launch": f + w, "launches": len(k["fetch"])}
+    stages = {}
+    for stage, subs in STAGE_KERNELS.items():
+        ks = [n for n in out_k if any(sub in n for sub in subs)]
+        if ks:
+            stages[stage] = {"kernels": ks,
+                             "bytes_per_call": sum(out_k[n]["bytes_per_launch"] for n in ks)}
+    d = {"workload": workload, "source_hash": kernel_source_hash(),
+         "copy_probe_bytes": COPY_PROBE_BYTES,
+         "copy_probe_measured": {"fetch": pf, "write": pw},
+         "scale": {"fetch": f_scale, "write": w_scale},
+         "kernels": out_k, "stages": stages, "commands": commands,
+         "note": ("FETCH_SIZE / WRITE_SIZE in KiB per dispatch (x1024), median over the "
+                  "dispatches of each kernel, each scaled by copy_probe_bytes / the counter's "
+                  "reading for one device-to-device copy of copy_probe_bytes")}
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    json.dump(d, open(path, "w"), indent=1)
+    print(json.dumps({k: v["bytes_per_call"] for k, v in stages.items()}))
 
 
 # --------------------------------------------------------------------------
@@ -146,6 +230,10 @@ def committed_traffic(workload: str, kernel: str):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload, {},
+                        args.commands)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path "
               "shards by sequence with no exchange, see the design notes", file=sys.stderr)
@@ -253,12 +341,24 @@ def main():
     names = ["indexer", "topk"] + [f"mla_l{l}" for l in range(wl.n_layers)]
     stage_bytes = [ab["indexer"], ab["topk"]] + [ab["mla_per_layer"]] * wl.n_layers
     mla_ms = float(np.sum(stage_ms[2:]))
-    kern = {"indexer": (float(stage_ms[0]), ab["indexer"], "indexer_mfma_kernel"),
-            "topk": (float(stage_ms[1]), ab["topk"], "topk_kernel"),
-            "sparse_mla": (mla_ms / wl.n_layers, ab["mla_per_layer"], "sparse_mla_bf16_kernel")}
+    kern = {"indexer": (float(stage_ms[0]), ab["indexer"], "dsa_indexer_scores",
+                        ab["flops_indexer"]),
+            "topk": (float(stage_ms[1]), ab["topk"], "dsa_topk", 0),
+            "sparse_mla": (mla_ms / wl.n_layers, ab["mla_per_layer"], "dsa_sparse_mla_fwd",
+                           ab["flops_mla_per_layer"])}
     dom = max(kern, key=lambda k: kern[k][0] * (wl.n_layers if k == "sparse_mla" else 1))
-    d_ms, d_bytes, d_sym = kern[dom]
-    achieved = d_bytes / (d_ms * 1e-3) / 1e9
+    d_ms, d_bytes, d_sym, d_flops = kern[dom]
+    # the dominant call against the roofline it is closer to: HBM bytes or bf16 MFMA flops
+    hbm_gbs = d_bytes / (d_ms * 1e-3) / 1e9
+    mfma_tfs = d_flops / (d_ms * 1e-3) / 1e12
+    mfma_bound = wl.mla_dtype == "bf16" and mfma_tfs / MFMA_BF16_PEAK_TFS > hbm_gbs / HBM_PEAK_GBS
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": mfma_tfs, "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": mfma_tfs / MFMA_BF16_PEAK_TFS,
+                "algorithmic_flops_per_launch": d_flops}
+    else:
+        roof = {"bound": "hbm", "achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": hbm_gbs / HBM_PEAK_GBS}
     line = {
         "metric": "sparse-decode query tokens/s at B=32,L=8K,topk=2048; achieved HBM GB/s",
         "value": T / (ms * 1e-3),
@@ -286,12 +386,18 @@ def main():
                    ("" if args.no_flush else " after a 1 GiB read that evicts the caches") +
                    ("; HIP graph replay of the captured step" if args.graph
                     else "; plain stream launches")),
-        "roofline": {"bound": "hbm", "kernel": d_sym, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": committed_traffic(wl.name, d_sym),
-                     "algorithmic_bytes_per_launch": d_bytes, "avg_launch_ms": d_ms},
+        "roofline": dict(roof, kernel=d_sym, kernels=STAGE_KERNELS[dom],
+                         traffic=committed_traffic(wl.name, dom),
+                         algorithmic_bytes_per_launch=d_bytes, avg_launch_ms=d_ms),
         "wall_s_timed_loop": wall,
     }
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -83,6 +83,29 @@ def test_indexshare_layers_reuse_one_topk(dev):
     assert not torch.equal(outs[0][0], outs[1][0])
 
 
+def test_mla_restart_on_late_large_logits(dev):
+    """Rows 64..95 of sequence 0 are scaled by 100, so their logits exceed the softmax
+    reference fixed by the split's first tile by far more than the 2^64 headroom: the
+    split is walked a second time from a raised reference, and the result is still the
+    oracle's. With k >= L every position is selected, so the scaled rows are in the
+    first split of row 0 (slots 0..127, tiles of 32) behind two ordinary tiles."""
+    wl = small_variant(BF16_DECODE, batch=2, lens=(600, 300), topk=1024)
+    inp_h = make_inputs(wl)
+    ps = wl.page_size
+    cache = inp_h.kv_cache[0]
+    for pos in range(64, 96):
+        page = int(inp_h.block_table[0, pos // ps])
+        cache[page, pos % ps] = (cache[page, pos % ps].float() * 100.0).to(cache.dtype)
+    inp = to_device(inp_h, dev)
+    host = host_view(inp_h)
+    scores, idx, outs = P.run_gpu(inp)
+    rows = list(range(inp.total_q))
+    P.check_invariants(inp, idx, wl.topk)
+    out, lse = outs[0]
+    assert torch.isfinite(out).all()
+    P.check_mla(inp, 0, idx, out, lse, rows, host)
+
+
 def test_block_table_permutation_invariance(dev):
     """Same logical caches under two different physical page layouts give identical outputs."""
     wl = small_variant(BF16_DECODE, batch=2, lens=(700, 1300))
