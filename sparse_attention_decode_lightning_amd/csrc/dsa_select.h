@@ -1,0 +1,213 @@
+// Exact block-wide top-k selection over scores held in registers ("GLM-5.2 on
+// vLLM Ascend: Request-to-Backend Inference Path", section "8. The SFA
+// backend, step by step": the indexer returns the 2,048 best token
+// positions).
+//
+// Order: larger score first; equal scores by lower position first; -0.0 is
+// folded into +0.0 so the two compare equal. Scores map to order-preserving
+// 32-bit keys, so the order is (key descending, position ascending).
+//
+// A block of NW waves holds candidates u * (64 NW) + tid (u < R) as keys in
+// registers.
+//  * Three radix levels (11, 11 and 10 bits) use three LDS histograms that are
+//    cleared before the first level, so a level costs one barrier: after it
+//    every wave scans the whole histogram itself and reaches the same digit.
+//    Bin b sits at word b + 4 (b / 32): lane l of a scanning wave owns bins
+//    [32 l, 32 l + 32) and reads them with 16-byte loads that no other lane of
+//    its group of eight shares a bank with.
+//  * The selection stops at the first level whose chosen bin is kept whole
+//    (its count equals what is still needed): the keys above the bin and all
+//    keys in it are then the top k. Continuous scores usually stop after two
+//    levels.
+//  * Ordered emit: positions run u-major, then wave, then lane, so per-u wave
+//    ballots of "above the bin" and "in the bin", one exclusive scan of the
+//    R x NW packed per-wave counts (done by every wave on its own) and a
+//    popcount below the lane give every kept candidate its slot in ascending
+//    position order, with no sort.
+#pragma once
+
+#include "dsa_device.h"
+
+namespace dsa {
+
+constexpr int kSelBins = 2048;                    // 11-bit digits
+constexpr int kSelBinsWords = kSelBins / 32 * 36;  // padded histogram
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  u = (u == 0x80000000u) ? 0u : u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int sel_bin(uint32_t b) { return (int)(b + 4 * (b >> 5)); }
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+// Scans over the 64 lanes of a wave without LDS: DPP row shifts scan each row
+// of 16 lanes (lanes shifted in from outside the row read 0), then the totals
+// of the other rows, read as scalars from lanes 0, 16, 32 and 48 (suffix) or
+// 15, 31, 47 (prefix), are added per row.
+// Suffix sum: lane l gets the total of lanes >= l (row_shl n: lane l reads l + n).
+__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
+  v += dpp_u32<0x101>(v);
+  v += dpp_u32<0x102>(v);
+  v += dpp_u32<0x104>(v);
+  v += dpp_u32<0x108>(v);
+  const uint32_t r1 = __builtin_amdgcn_readlane(v, 16), r2 = __builtin_amdgcn_readlane(v, 32),
+                 r3 = __builtin_amdgcn_readlane(v, 48);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row == 0 ? r1 + r2 + r3 : row == 1 ? r2 + r3 : row == 2 ? r3 : 0u);
+}
+
+// Inclusive prefix sum: lane l gets the total of lanes <= l (row_shr n: lane l reads l - n).
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v) {
+  v += dpp_u32<0x111>(v);
+  v += dpp_u32<0x112>(v);
+  v += dpp_u32<0x114>(v);
+  v += dpp_u32<0x118>(v);
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+                 r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row == 3 ? r0 + r1 + r2 : row == 2 ? r0 + r1 : row == 1 ? r0 : 0u);
+}
+
+// Every lane of the calling wave: the digit of the need-th largest candidate
+// in a histogram of NB bins (sel_bin layout), how many candidates with that
+// digit are still needed, and how many there are. Two stages, neither with a
+// serial search: lane totals of 32 (16) bins and their suffix sums find the
+// lane L whose bins hold the crossing; then lane i < 32 (16) reads bin
+// 32 L + i, and a second suffix sum and ballot find the bin.
+template <int NB>
+__device__ __forceinline__ void wave_pick(const uint32_t *hist, uint32_t need, uint32_t &digit,
+                                          uint32_t &rest, uint32_t &count) {
+  constexpr int per = NB / 64;
+  const int lane = threadIdx.x & 63;
+  const u32x4_t *src = reinterpret_cast<const u32x4_t *>(hist + sel_bin(per * lane));
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < per / 4; ++i) {
+    const u32x4_t q = src[i];
+    mine += (q.x + q.y) + (q.z + q.w);
+  }
+  const uint32_t suf = wave_suffix_sum(mine);
+  const uint32_t above = suf - mine;
+  const uint64_t who = __ballot(above < need && suf >= need);
+  const int L = who != 0ull ? __ffsll((unsigned long long)who) - 1 : 0;
+  const uint32_t above_l = __builtin_amdgcn_readlane(above, L);
+  const uint32_t hb = lane < per ? hist[sel_bin(per * L + lane)] : 0u;
+  const uint32_t s2 = wave_suffix_sum(hb);  // lanes >= per add 0
+  const uint64_t hit = __ballot(lane < per && above_l + s2 >= need);
+  const int i = hit != 0ull ? 63 - __clzll(hit) : 0;
+  const uint32_t s_i = __builtin_amdgcn_readlane(s2, i), h_i = __builtin_amdgcn_readlane(hb, i);
+  digit = (uint32_t)(per * L + i);
+  count = h_i;
+  rest = need - (above_l + s_i - h_i);
+}
+
+// LDS of one selection: the three histograms, the packed per-(u, wave)
+// counts and each wave's private copy of their exclusive scan.
+template <int NW, int R>
+struct alignas(16) SelectShared {
+  uint32_t hist[3][kSelBinsWords];
+  uint32_t cnt[R * NW];
+  uint32_t scan[NW][R * NW];
+};
+
+// Zero the histograms (no barrier: select_run starts with one).
+template <int NW, int R>
+__device__ __forceinline__ void select_clear(SelectShared<NW, R> &sh) {
+  u32x4_t *h = reinterpret_cast<u32x4_t *>(&sh.hist[0][0]);
+  for (int i = threadIdx.x; i < 3 * kSelBinsWords / 4; i += NW * kWave) h[i] = u32x4_t{0u, 0u, 0u, 0u};
+}
+
+// The k best of the n candidates u * (64 NW) + tid (< n, and n > k): emit(u,
+// slot) is called once for every kept candidate, with its slot in [0, k) of
+// the ascending-position list. Every thread of the block must call it.
+template <int NW, int R, typename Emit>
+__device__ __forceinline__ void select_run(const uint32_t (&key)[R], int n, int k,
+                                           SelectShared<NW, R> &sh, Emit emit) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  auto valid = [&](int u) { return u * NW * kWave + tid < n; };
+  __syncthreads();  // histograms cleared
+
+  // level 1: bits 31..21
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+    if (valid(u)) atomicAdd(&sh.hist[0][sel_bin(key[u] >> 21)], 1u);
+  __syncthreads();
+  uint32_t d, need, count;
+  wave_pick<kSelBins>(sh.hist[0], (uint32_t)k, d, need, count);
+  uint32_t prefix = d << 21;
+  int shift = 21;
+  if (need != count) {
+    // level 2: bits 20..10 of the keys in the chosen bin
+#pragma unroll
+    for (int u = 0; u < R; ++u)
+      if (valid(u) && (key[u] >> 21) == d)
+        atomicAdd(&sh.hist[1][sel_bin((key[u] >> 10) & 2047u)], 1u);
+    __syncthreads();
+    wave_pick<kSelBins>(sh.hist[1], need, d, need, count);
+    prefix |= d << 10;
+    shift = 10;
+    if (need != count) {
+      // level 3: bits 9..0
+#pragma unroll
+      for (int u = 0; u < R; ++u)
+        if (valid(u) && (key[u] >> 10) == (prefix >> 10))
+          atomicAdd(&sh.hist[2][sel_bin(key[u] & 1023u)], 1u);
+      __syncthreads();
+      wave_pick<kSelBins / 2>(sh.hist[2], need, d, need, count);
+      prefix |= d;
+      shift = 0;
+    }
+  }
+  const uint32_t tp = prefix >> shift;
+
+  // ordered emit: "above" = keys above the chosen bin, "in" = keys in it, of
+  // which the first `need` (by position) are kept
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const uint64_t mg = __ballot(valid(u) && (key[u] >> shift) > tp);
+    const uint64_t me = __ballot(valid(u) && (key[u] >> shift) == tp);
+    if (lane == 0)
+      sh.cnt[u * NW + wv] = ((uint32_t)__popcll(mg) << 16) | (uint32_t)__popcll(me);
+  }
+  __syncthreads();
+  {
+    // exclusive scan of the R * NW packed counts in (u, wave) order, by every
+    // wave into its own copy
+    constexpr int per = (R * NW + 63) / 64;
+    uint32_t c[per], tot = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      c[i] = per * lane + i < R * NW ? sh.cnt[per * lane + i] : 0u;
+      tot += c[i];
+    }
+    uint32_t run = wave_prefix_sum(tot) - tot;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      if (per * lane + i < R * NW) sh.scan[wv][per * lane + i] = run;
+      run += c[i];
+    }
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const uint32_t off = sh.scan[wv][u * NW + wv];
+    const bool gt = valid(u) && (key[u] >> shift) > tp;
+    const bool eq = valid(u) && (key[u] >> shift) == tp;
+    const uint64_t mg = __ballot(gt);
+    const uint64_t me = __ballot(eq);
+    const uint32_t gt_before = (off >> 16) + (uint32_t)__popcll(mg & below);
+    const uint32_t eq_before = (off & 0xFFFFu) + (uint32_t)__popcll(me & below);
+    uint32_t slot = (uint32_t)k;
+    if (gt) slot = gt_before + min(eq_before, need);
+    else if (eq && eq_before < need) slot = gt_before + eq_before;
+    if (slot < (uint32_t)k) emit(u, (int)slot);
+  }
+}
+
+}  // namespace dsa

@@ -25,6 +25,7 @@
 // lists are concatenated.
 #include "dsa_device.h"
 #include "dsa_internal.h"
+#include "dsa_select.h"
 
 namespace dsa {
 namespace {
@@ -33,12 +34,6 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kChunk = 32768;  // candidates per workgroup (keys cached in LDS)
 constexpr int kBinsA = 2048;   // 11-bit digits: key bits 31..21, 20..10, then 9..0
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  u = (u == 0x80000000u) ? 0u : u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 // Histogram bins are padded by one word per 64, so that a lane reading 64
 // consecutive bins hits a different bank than its neighbours.
@@ -314,112 +309,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
   ordered_emit(s_keys, n, tau, need, sh, pos_of, out, nullptr);
 }
 
-// Rows of at most R * 512 candidates (every decode row of up to 16K tokens):
-// 512 threads, thread tid holding candidates u * 512 + tid (u < R) as keys in
-// registers. The row's scores are requested before its length is known (every
-// load stays below max_seq_len <= ld) and masked afterwards.
-//  * The three radix histograms (11, 11 and 10 bits) sit side by side in LDS
-//    and are cleared before the first pass, so a pass costs one barrier: after
-//    it every wave scans the whole histogram itself and reaches the same digit.
-//    Bin b of a histogram sits at word b + 4 (b / 32): lane l of a scanning
-//    wave owns bins [32 l, 32 l + 32) and reads them with 16-byte loads that
-//    no other lane of its group of eight shares a bank with.
-//  * The selection stops at the first level whose chosen bin is kept whole
-//    (its count equals what is still needed): the keys above the bin and all
-//    keys in it are then the top k. Continuous scores usually stop after two
-//    passes.
-//  * Ordered emit: positions run u-major, then wave, then lane, so per-u wave
-//    ballots of "above the bin" and "in the bin", one exclusive scan of the
-//    R x 8 packed per-wave counts (done by every wave on its own) and a
-//    popcount below the lane give every kept candidate its slot in ascending
-//    position order.
-constexpr int kRegThreads = 512;
-constexpr int kRegWaves = kRegThreads / kWave;
-constexpr int kRegBinsWords = kBinsA / 32 * 36;
+constexpr int kRegThreads = 1024;
 
-__device__ __forceinline__ int reg_bin(uint32_t b) { return (int)(b + 4 * (b >> 5)); }
-
-template <int R>
-struct alignas(16) TopkRegShared {
-  uint32_t hist[3][kRegBinsWords];
-  uint32_t cnt[R * kRegWaves];
-  uint32_t scan[kRegWaves][R * kRegWaves];
-};
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
-}
-
-// Scans over the 64 lanes of a wave without LDS: DPP row shifts scan each row
-// of 16 lanes (lanes shifted in from outside the row read 0), then the totals
-// of the other rows, read as scalars from lanes 0, 16, 32 and 48 (suffix) or
-// 15, 31, 47 (prefix), are added per row.
-// Suffix sum: lane l gets the total of lanes >= l (row_shl n: lane l reads l + n).
-__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
-  v += dpp_u32<0x101>(v);
-  v += dpp_u32<0x102>(v);
-  v += dpp_u32<0x104>(v);
-  v += dpp_u32<0x108>(v);
-  const uint32_t r1 = __builtin_amdgcn_readlane(v, 16), r2 = __builtin_amdgcn_readlane(v, 32),
-                 r3 = __builtin_amdgcn_readlane(v, 48);
-  const int row = (threadIdx.x & 63) >> 4;
-  return v + (row == 0 ? r1 + r2 + r3 : row == 1 ? r2 + r3 : row == 2 ? r3 : 0u);
-}
-
-// Inclusive prefix sum: lane l gets the total of lanes <= l (row_shr n: lane l reads l - n).
-__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v) {
-  v += dpp_u32<0x111>(v);
-  v += dpp_u32<0x112>(v);
-  v += dpp_u32<0x114>(v);
-  v += dpp_u32<0x118>(v);
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
-                 r2 = __builtin_amdgcn_readlane(v, 47);
-  const int row = (threadIdx.x & 63) >> 4;
-  return v + (row == 3 ? r0 + r1 + r2 : row == 2 ? r0 + r1 : row == 1 ? r0 : 0u);
-}
-
-// Every lane of the calling wave: the digit of the need-th largest candidate
-// in a histogram of NB bins (reg_bin layout), how many candidates with that
-// digit are still needed, and how many there are. Two stages, neither with a
-// serial search: lane totals of 32 (16) bins and their suffix sums find the
-// lane L whose bins hold the crossing; then lane i < 32 (16) reads bin
-// 32 L + i, and a second suffix sum and ballot find the bin.
-template <int NB>
-__device__ __forceinline__ void wave_pick(const uint32_t *hist, uint32_t need, uint32_t &digit,
-                                          uint32_t &rest, uint32_t &count) {
-  constexpr int per = NB / 64;
-  const int lane = threadIdx.x & 63;
-  const u32x4_t *src = reinterpret_cast<const u32x4_t *>(hist + reg_bin(per * lane));
-  uint32_t mine = 0;
-#pragma unroll
-  for (int i = 0; i < per / 4; ++i) {
-    const u32x4_t q = src[i];
-    mine += (q.x + q.y) + (q.z + q.w);
-  }
-  const uint32_t suf = wave_suffix_sum(mine);
-  const uint32_t above = suf - mine;
-  const uint64_t who = __ballot(above < need && suf >= need);
-  const int L = who != 0ull ? __ffsll((unsigned long long)who) - 1 : 0;
-  const uint32_t above_l = __builtin_amdgcn_readlane(above, L);
-  const uint32_t hb = lane < per ? hist[reg_bin(per * L + lane)] : 0u;
-  const uint32_t s2 = wave_suffix_sum(hb);  // lanes >= per add 0
-  const uint64_t hit = __ballot(lane < per && above_l + s2 >= need);
-  const int i = hit != 0ull ? 63 - __clzll(hit) : 0;
-  const uint32_t s_i = __builtin_amdgcn_readlane(s2, i), h_i = __builtin_amdgcn_readlane(hb, i);
-  digit = (uint32_t)(per * L + i);
-  count = h_i;
-  rest = need - (above_l + s_i - h_i);
-}
-
-template <int R>
-__global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(
+// Rows of at most R * NT candidates (every decode row of up to 16K tokens):
+// NT threads, thread tid holding candidates u * NT + tid (u < R) as keys in
+// registers, selected by select_run (three pre-cleared LDS histograms, one
+// barrier per radix level, per-wave digit picks, an early stop once the chosen
+// bin is kept whole, a ballot-based ordered emit). The row's scores are
+// requested before its length is known (every load stays below
+// max_seq_len <= ld) and masked afterwards.
+template <int NT, int R>
+__global__ __launch_bounds__(NT) void topk_reg_kernel(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
     int total_q, int max_seq_len, const float *__restrict__ scores, int64_t ld, int k,
     int32_t *__restrict__ indices) {
-  __shared__ TopkRegShared<R> sh;
+  constexpr int kRegThreads = NT;
+  __shared__ SelectShared<NT / kWave, R> sh;
   const int row = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x;
   const float *src = scores + (int64_t)row * ld;
   float v[R];
 #pragma unroll
@@ -427,10 +334,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(
     const int i = u * kRegThreads + tid;
     v[u] = i < max_seq_len ? src[i] : 0.0f;
   }
-  {
-    u32x4_t *h = reinterpret_cast<u32x4_t *>(&sh.hist[0][0]);
-    for (int i = tid; i < 3 * kRegBinsWords / 4; i += kRegThreads) h[i] = u32x4_t{0u, 0u, 0u, 0u};
-  }
+  select_clear(sh);
   const int n = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row).t + 1;
   int32_t *out = indices + (int64_t)row * k;
   if (n <= k) {
@@ -440,76 +344,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(
   uint32_t key[R];
 #pragma unroll
   for (int u = 0; u < R; ++u) key[u] = order_key(v[u]);
-  auto valid = [&](int u) { return u * kRegThreads + tid < n; };
-  __syncthreads();
-
-  // level 1: bits 31..21
-#pragma unroll
-  for (int u = 0; u < R; ++u)
-    if (valid(u)) atomicAdd(&sh.hist[0][reg_bin(key[u] >> 21)], 1u);
-  __syncthreads();
-  uint32_t d, need, count;
-  wave_pick<kBinsA>(sh.hist[0], (uint32_t)k, d, need, count);
-  uint32_t prefix = d << 21;
-  int shift = 21;
-  if (need != count) {
-    // level 2: bits 20..10 of the keys in the chosen bin
-#pragma unroll
-    for (int u = 0; u < R; ++u)
-      if (valid(u) && (key[u] >> 21) == d) atomicAdd(&sh.hist[1][reg_bin((key[u] >> 10) & 2047u)], 1u);
-    __syncthreads();
-    wave_pick<kBinsA>(sh.hist[1], need, d, need, count);
-    prefix |= d << 10;
-    shift = 10;
-    if (need != count) {
-      // level 3: bits 9..0
-#pragma unroll
-      for (int u = 0; u < R; ++u)
-        if (valid(u) && (key[u] >> 10) == (prefix >> 10))
-          atomicAdd(&sh.hist[2][reg_bin(key[u] & 1023u)], 1u);
-      __syncthreads();
-      wave_pick<kBinsA / 2>(sh.hist[2], need, d, need, count);
-      prefix |= d;
-      shift = 0;
-    }
-  }
-  const uint32_t tp = prefix >> shift;
-
-  // ordered emit: "above" = keys above the chosen bin, "in" = keys in it, of
-  // which the first `need` (by position) are kept
-  uint64_t mg[R], me[R];
-#pragma unroll
-  for (int u = 0; u < R; ++u) {
-    mg[u] = __ballot(valid(u) && (key[u] >> shift) > tp);
-    me[u] = __ballot(valid(u) && (key[u] >> shift) == tp);
-    if (lane == 0)
-      sh.cnt[u * kRegWaves + wv] = ((uint32_t)__popcll(mg[u]) << 16) | (uint32_t)__popcll(me[u]);
-  }
-  __syncthreads();
-  {
-    // exclusive scan of the R * 8 packed counts in (u, wave) order, by every
-    // wave into its own copy
-    constexpr int per = R * kRegWaves / 64;
-    uint32_t c[per], tot = 0;
-#pragma unroll
-    for (int i = 0; i < per; ++i) { c[i] = sh.cnt[per * lane + i]; tot += c[i]; }
-    uint32_t run = wave_prefix_sum(tot) - tot;
-#pragma unroll
-    for (int i = 0; i < per; ++i) { sh.scan[wv][per * lane + i] = run; run += c[i]; }
-  }
-  const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int u = 0; u < R; ++u) {
-    const uint32_t off = sh.scan[wv][u * kRegWaves + wv];
-    const bool gt = (mg[u] >> lane) & 1ull;
-    const bool eq = (me[u] >> lane) & 1ull;
-    const uint32_t gt_before = (off >> 16) + (uint32_t)__popcll(mg[u] & below);
-    const uint32_t eq_before = (off & 0xFFFFu) + (uint32_t)__popcll(me[u] & below);
-    uint32_t slot = (uint32_t)k;
-    if (gt) slot = gt_before + min(eq_before, need);
-    else if (eq && eq_before < need) slot = gt_before + eq_before;
-    if (slot < (uint32_t)k) out[slot] = u * kRegThreads + tid;
-  }
+  select_run(key, n, k, sh, [&](int u, int slot) { out[slot] = u * kRegThreads + tid; });
 }
 
 int chunks_of(int32_t max_seq_len) { return (max_seq_len + kChunk - 1) / kChunk; }
@@ -536,8 +371,9 @@ bool topk_supported(int32_t max_seq_len, int32_t k) {
 hipError_t launch_topk(const BatchArgs &bt, const float *scores, int64_t ld, int32_t k,
                        int32_t *indices, void *workspace, size_t, hipStream_t stream) {
   if (bt.total_q == 0) return hipSuccess;
-  if (bt.max_seq_len <= 32 * kRegThreads) {
-    auto kernel = bt.max_seq_len <= 16 * kRegThreads ? topk_reg_kernel<16> : topk_reg_kernel<32>;
+  if (bt.max_seq_len <= 16 * kRegThreads) {
+    auto kernel = bt.max_seq_len <= 8 * kRegThreads ? topk_reg_kernel<kRegThreads, 8>
+                                                    : topk_reg_kernel<kRegThreads, 16>;
     hipLaunchKernelGGL(kernel, dim3(bt.total_q), dim3(kRegThreads), 0, stream, bt.seq_lens,
                        bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, scores, ld, k, indices);
     return hipGetLastError();
