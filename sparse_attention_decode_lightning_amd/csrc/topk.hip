@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
 
 constexpr int kRegThreads = 1024;
 
-// Rows of at most R * NT candidates (every decode row of up to 16K tokens):
+// Rows of at most R * NT candidates (every row of up to 32K tokens):
 // NT threads, thread tid holding candidates u * NT + tid (u < R) as keys in
 // registers, selected by select_run (three pre-cleared LDS histograms, one
 // barrier per radix level, per-wave digit picks, an early stop once the chosen
@@ -347,6 +347,98 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(
   select_run(key, n, k, sh, [&](int u, int slot) { out[slot] = u * kRegThreads + tid; });
 }
 
+// Rows longer than one register block (32K): two phases on the same selection.
+// Phase 1 selects the top-k of every 16K-position chunk of a row (one
+// 1024-thread workgroup per row and chunk) and writes the chunk's survivors,
+// keys and positions, in ascending position order to slots [c k, c k + m_c)
+// of the row's workspace, m_c = min(k, candidates of the chunk). Phase 2 (one
+// workgroup per row) selects among the nc * k slots, slots past a chunk's m_c
+// taking key 0 (below every score's key), so they are never kept. This is
+// exact: a position in the row's top-k is also in its chunk's top-k under the
+// same order, and slot order is position order among the survivors, so ties
+// still go to the lower position.
+constexpr int kSplitChunk = 16 * kRegThreads;    // phase-1 chunk: 1024 threads x 16 keys
+constexpr int kSplitCands = 32 * kRegThreads;    // phase-2 slots: 1024 threads x 32 keys
+
+int split_chunks(int32_t max_seq_len) { return (max_seq_len + kSplitChunk - 1) / kSplitChunk; }
+
+bool split_path(int32_t max_seq_len, int32_t k) {
+  return max_seq_len > 32 * kRegThreads && (int64_t)split_chunks(max_seq_len) * k <= kSplitCands;
+}
+
+__global__ __launch_bounds__(kRegThreads) void topk_chunk_kernel(
+    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
+    int total_q, int max_seq_len, const float *__restrict__ scores, int64_t ld, int k, int nc,
+    uint32_t *__restrict__ ws_key, int32_t *__restrict__ ws_pos) {
+  constexpr int R = kSplitChunk / kRegThreads;
+  __shared__ SelectShared<kRegThreads / kWave, R> sh;
+  const int c = blockIdx.x, row = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int base = c * kSplitChunk;
+  const float *src = scores + (int64_t)row * ld + base;
+  float v[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int i = u * kRegThreads + tid;
+    v[u] = base + i < max_seq_len ? src[i] : 0.0f;
+  }
+  select_clear(sh);
+  const int n = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row).t + 1;
+  const int m = min(max(n - base, 0), kSplitChunk);  // candidates of this chunk
+  uint32_t *okey = ws_key + ((int64_t)row * nc + c) * k;
+  int32_t *opos = ws_pos + ((int64_t)row * nc + c) * k;
+  uint32_t key[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) key[u] = order_key(v[u]);
+  if (m <= k) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int i = u * kRegThreads + tid;
+      if (i < m) {
+        okey[i] = key[u];
+        opos[i] = base + i;
+      }
+    }
+    return;
+  }
+  select_run(key, m, k, sh, [&](int u, int slot) {
+    okey[slot] = key[u];
+    opos[slot] = base + u * kRegThreads + tid;
+  });
+}
+
+template <int R>
+__global__ __launch_bounds__(kRegThreads) void topk_split_merge_kernel(
+    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
+    int total_q, int max_seq_len, int k, FastDiv kdiv, int nc, const uint32_t *__restrict__ ws_key,
+    const int32_t *__restrict__ ws_pos, int32_t *__restrict__ indices) {
+  __shared__ SelectShared<kRegThreads / kWave, R> sh;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  select_clear(sh);
+  const int n = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row).t + 1;
+  int32_t *out = indices + (int64_t)row * k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kRegThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const uint32_t *ikey = ws_key + (int64_t)row * nc * k;
+  const int32_t *ipos = ws_pos + (int64_t)row * nc * k;
+  uint32_t key[R];
+  int32_t pos[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int j = u * kRegThreads + tid;
+    const int c = (int)fast_div((uint32_t)j, kdiv);
+    const int s = j - c * k;
+    const int m = min(min(max(n - c * kSplitChunk, 0), kSplitChunk), k);  // survivors of chunk c
+    const bool ok = j < nc * k && s < m;
+    key[u] = ok ? ikey[j] : 0u;
+    pos[u] = ok ? ipos[j] : -1;
+  }
+  select_run(key, nc * k, k, sh, [&](int u, int slot) { out[slot] = pos[u]; });
+}
+
 int chunks_of(int32_t max_seq_len) { return (max_seq_len + kChunk - 1) / kChunk; }
 
 bool two_phase(int32_t max_seq_len) { return max_seq_len > kChunk; }
@@ -358,12 +450,15 @@ hipError_t set_lds(const void *fn, size_t bytes) {
 }  // namespace
 
 size_t topk_workspace_bytes(int32_t total_q, int32_t max_seq_len, int32_t k) {
-  if (!two_phase(max_seq_len) || total_q < 1 || k < 1) return 0;
-  return (size_t)total_q * chunks_of(max_seq_len) * k * (sizeof(uint32_t) + sizeof(int32_t));
+  if (total_q < 1 || k < 1) return 0;
+  const size_t per = (size_t)total_q * k * (sizeof(uint32_t) + sizeof(int32_t));
+  if (split_path(max_seq_len, k)) return per * split_chunks(max_seq_len);
+  if (!two_phase(max_seq_len)) return 0;
+  return per * chunks_of(max_seq_len);
 }
 
 bool topk_supported(int32_t max_seq_len, int32_t k) {
-  if (!two_phase(max_seq_len)) return true;
+  if (!two_phase(max_seq_len) || split_path(max_seq_len, k)) return true;
   const int nc = chunks_of(max_seq_len);
   return nc < 64 && (int64_t)nc * (k < kChunk ? k : kChunk) <= kChunk;
 }
@@ -371,15 +466,34 @@ bool topk_supported(int32_t max_seq_len, int32_t k) {
 hipError_t launch_topk(const BatchArgs &bt, const float *scores, int64_t ld, int32_t k,
                        int32_t *indices, void *workspace, size_t, hipStream_t stream) {
   if (bt.total_q == 0) return hipSuccess;
-  if (bt.max_seq_len <= 16 * kRegThreads) {
-    auto kernel = bt.max_seq_len <= 8 * kRegThreads ? topk_reg_kernel<kRegThreads, 8>
-                                                    : topk_reg_kernel<kRegThreads, 16>;
+  if (bt.max_seq_len <= 32 * kRegThreads) {
+    auto kernel = bt.max_seq_len <= 8 * kRegThreads    ? topk_reg_kernel<kRegThreads, 8>
+                  : bt.max_seq_len <= 16 * kRegThreads ? topk_reg_kernel<kRegThreads, 16>
+                                                       : topk_reg_kernel<kRegThreads, 32>;
     hipLaunchKernelGGL(kernel, dim3(bt.total_q), dim3(kRegThreads), 0, stream, bt.seq_lens,
                        bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, scores, ld, k, indices);
     return hipGetLastError();
   }
-  const size_t lds = (size_t)kChunk * sizeof(uint32_t);
   hipError_t e;
+  if (split_path(bt.max_seq_len, k)) {
+    const int nc = split_chunks(bt.max_seq_len);
+    if (bt.total_q > 65535) return hipErrorInvalidConfiguration;
+    uint32_t *ws_key = static_cast<uint32_t *>(workspace);
+    int32_t *ws_pos = reinterpret_cast<int32_t *>(ws_key + (size_t)bt.total_q * nc * k);
+    hipLaunchKernelGGL(topk_chunk_kernel, dim3(nc, bt.total_q), dim3(kRegThreads), 0, stream,
+                       bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, scores, ld, k,
+                       nc, ws_key, ws_pos);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t cands = (int64_t)nc * k;
+    auto merge = cands <= 8 * kRegThreads    ? topk_split_merge_kernel<8>
+                 : cands <= 16 * kRegThreads ? topk_split_merge_kernel<16>
+                                             : topk_split_merge_kernel<32>;
+    hipLaunchKernelGGL(merge, dim3(bt.total_q), dim3(kRegThreads), 0, stream, bt.seq_lens,
+                       bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, k,
+                       make_fast_div((uint32_t)k), nc, ws_key, ws_pos, indices);
+    return hipGetLastError();
+  }
+  const size_t lds = (size_t)kChunk * sizeof(uint32_t);
   if (!two_phase(bt.max_seq_len)) {
     if ((e = set_lds((const void *)topk_rows_kernel<false>, lds)) != hipSuccess) return e;
     hipLaunchKernelGGL(topk_rows_kernel<false>, dim3(bt.total_q), dim3(kTopkThreads), lds, stream,
