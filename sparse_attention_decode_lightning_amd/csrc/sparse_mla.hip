@@ -550,8 +550,9 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
 
 // Merge the splits of one row: 256 threads = 4 heads x 64 threads x 8 dims.
 // O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, lse = M ln 2 + ln(sum ...).
-// Splits are taken eight at a time with every load of the eight issued before
-// any is used.
+// One pass: splits are taken eight at a time with every load of the eight
+// issued before any is used, and the running sums move to each chunk's new
+// maximum (one round trip for up to eight splits).
 __global__ __launch_bounds__(256) void mla_combine_kernel(int n_splits,
                                                           const float *__restrict__ ws_acc,
                                                           const float *__restrict__ ws_ml,
@@ -563,16 +564,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(int n_splits,
   const int d0 = (threadIdx.x & 63) * 8;
   const float *ml = ws_ml + ((int64_t)row * n_splits * kH + head) * 2;  // split s at + s*kH*2
   const float *acc = ws_acc + (((int64_t)row * n_splits * kH + head) * kDL + d0);  // + s*kH*kDL
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < n_splits; s0 += kU) {
-    float m[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) m[u] = s0 + u < n_splits ? ml[(s0 + u) * kH * 2] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) M = fmaxf(M, m[u]);
-  }
-  const float Mu = M == -INFINITY ? 0.0f : M;
-  float Lsum = 0.0f;
+  float M = -INFINITY, Lsum = 0.0f;
   f32x4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int s0 = 0; s0 < n_splits; s0 += kU) {
     float m[kU], l[kU];
@@ -586,13 +578,22 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(int n_splits,
       x0[u] = in ? *reinterpret_cast<const f32x4_t *>(src) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       x1[u] = in ? *reinterpret_cast<const f32x4_t *>(src + 4) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    float Mc = M;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) Mc = fmaxf(Mc, m[u]);
+    if (Mc == -INFINITY) continue;  // nothing valid yet
+    const float rescale = exp2f(M - Mc);  // 0 while M is -inf
+    Lsum *= rescale;
+    a0 *= rescale;
+    a1 *= rescale;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const float wgt = exp2f(m[u] - Mu);
+      const float wgt = exp2f(m[u] - Mc);
       Lsum += wgt * l[u];
       a0 += wgt * x0[u];
       a1 += wgt * x1[u];
     }
+    M = Mc;
   }
   const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
   float *dst = out + (((int64_t)row * kH + head) * kDL + d0);
