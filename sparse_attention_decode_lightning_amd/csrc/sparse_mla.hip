@@ -412,6 +412,21 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
+
+    // Value operands (transposed reads, two per 16-dim tile nt) run kVAhead
+    // tiles ahead of their MFMAs; the first kVAhead go out before the softmax
+    // so their latency hides under it.
+    auto vread = [&](int nt) -> u32x4_t {
+      const lds_u8 *vp = tb + v_off[nt & 7] + 256 * (nt >> 3);
+      const uint2 v0 = lds_read_tr16(vp);
+      const uint2 v1 = lds_read_tr16(vp + 16 * kRowBytes);
+      return u32x4_t{v0.x, v0.y, v1.x, v1.y};
+    };
+    constexpr int kVAhead = 6;
+    u32x4_t vbuf[32];
+#pragma unroll
+    for (int nt = 0; nt < kVAhead; ++nt) vbuf[nt] = vread(nt);
+    __builtin_amdgcn_sched_barrier(0);
     if (vmask != 0xFFFFFFFFu) {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
@@ -459,34 +474,18 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
         pa[2 * m + h] = hi;
         pl[2 * m + h] = pack_bf16x2(r0, r1);
       }
-    // value operands read one tile ahead of their MFMA
-    auto vread = [&](int nt) -> u32x4_t {
-      const lds_u8 *vp = tb + v_off[nt & 7] + 256 * (nt >> 3);
-      const uint2 v0 = lds_read_tr16(vp);
-      const uint2 v1 = lds_read_tr16(vp + 16 * kRowBytes);
-      return u32x4_t{v0.x, v0.y, v1.x, v1.y};
-    };
-    // value operands run kVAhead tiles ahead of their MFMAs
-    constexpr int kVAhead = 4;
-    u32x4_t vbuf[32];
-#pragma unroll
-    for (int nt = 0; nt < kVAhead; ++nt) vbuf[nt] = vread(nt);
+    // PV in a fixed order: each pair of MFMAs is preceded by the reads of
+    // the tile kVAhead further on. (Left to itself the scheduler sinks every
+    // read to just before its MFMAs, which exposes the whole LDS latency once
+    // per pair.)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int nt = 0; nt < 32; ++nt) {
       if (nt + kVAhead < 32) vbuf[nt + kVAhead] = vread(nt + kVAhead);
       o[nt] = mfma_16x16x32_bf16(pa, vbuf[nt], o[nt]);
       o[nt] = mfma_16x16x32_bf16(pl, vbuf[nt], o[nt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // issue order: the first 2 * kVAhead value reads overlap the softmax
-    // above; then two reads per pair of MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 40, 0);
-#pragma unroll
-    for (int i = 0; i < 32 - kVAhead; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kVAhead, 0);
   };
 
   // Passes over the split: normally one. A pass in which some tile
