@@ -212,24 +212,36 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
   const int32_t *idx_row = indices + (int64_t)row * k + slot_begin;
 
   // The query block of heads 16wv..16wv+15, the B operand of the logits:
-  // lane (g, j) holds head 16wv + j, dims 32s + 8g .. +8. Issued first: it
-  // lands while the row table's two dependent round trips below are in flight.
+  // lane (g, j) holds head 16wv + j, dims 32s + 8g .. +8. The first split of
+  // a row loads it at once, beside the row table's round trips; the other
+  // splits (same XCD) load it once their table is built, from the L2 that
+  // the first one filled, so the row's HBM reads of it are not repeated.
   u32x4_t qf[kSteps];
-  {
-    const uint16_t *qp = q + ((int64_t)row * kH + 16 * wv + j) * kD + 8 * g;
+  const uint16_t *qp = q + ((int64_t)row * kH + 16 * wv + j) * kD + 8 * g;
+  const bool q_first = split == 0;
+  if (q_first) {
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) qf[s] = ldg16(qp + 32 * s);
   }
 
   // Row table, first round trip: the selected positions of this thread's
   // entries (entry e covers slot kMlaThreads e + tid of the split), and in
-  // parallel the row's sequence and causal position.
+  // parallel the row's sequence and causal position. Every lane loads from
+  // an address inside the split (slots past it read its last entry; the
+  // table below drops them), so the loads need no branch: a load under a
+  // lane mask ends in a wait for all loads before the next one, which would
+  // serialize them. Nothing uses the values before the row's metadata
+  // arrives, so both land in one round trip.
   constexpr int kEntries = kMaxRowsPerSplit / kMlaThreads;
   int pos[kEntries];
 #pragma unroll
-  for (int e = 0; e < kEntries; ++e) {
-    const int i = e * kMlaThreads + tid;
-    pos[e] = i < nrows ? idx_row[i] : -1;
+  for (int e = 0; e < kEntries; ++e) pos[e] = -1;
+  if (nrows > 0) {
+#pragma unroll
+    for (int e = 0; e < kEntries; ++e) {
+      const int i = e * kMlaThreads + tid;
+      pos[e] = idx_row[min(i, nrows - 1)];
+    }
   }
   const RowInfo ri = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row);
   const int b = ri.b, t = ri.t;
@@ -237,7 +249,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
   // Second round trip: the page of every entry (positions clamped into
   // [0, t] so the reads stay inside the row's table whatever a slot holds;
   // slots outside it are masked below) and the page of position 0 (the
-  // stand-in row of masked slots).
+  // stand-in row of masked slots); again without a branch per load.
   int page[kEntries];
   int page0 = 0;
   if (t >= 0) {
@@ -245,7 +257,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
 #pragma unroll
     for (int e = 0; e < kEntries; ++e) {
       const int p = min(max(pos[e], 0), t);
-      page[e] = e * kMlaThreads + tid < ntiles * kTileN ? bt_row[fast_div((uint32_t)p, pdiv)] : 0;
+      page[e] = bt_row[fast_div((uint32_t)p, pdiv)];
     }
     page0 = bt_row[0];
   }
@@ -352,9 +364,14 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
   float m_run = -INFINITY, l_run = 0.0f;  // head 16wv + j; l_run covers this lane's rows
   bool overflow = false;
 
+  if (!q_first) {
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) qf[s] = ldg16(qp + 32 * s);
+  }
   if (tid < kMlaWaves) s_over[tid] = 0;
   // every compiler-visible load (query block, row table) has landed before the
-  // first direct copies, which the compiler does not count
+  // first direct copies, which the compiler does not count (a load of its own
+  // still in flight would make it wait for all of them inside the tile loop)
   __builtin_amdgcn_s_waitcnt(0x0070);
   __syncthreads();  // row table visible
 
@@ -494,8 +511,8 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
   // one is at most 2^kHeadroom), then the split is walked again from the
   // raised references. Not leaving the tile loop early keeps the
   // accumulators in the registers the MFMAs write.
+  for (int tile = 0; tile < min(ntiles, kStages - 1); ++tile) gather(tile);
   for (;;) {
-    for (int tile = 0; tile < min(ntiles, kStages - 1); ++tile) gather(tile);
     for (int tile = 0; tile < ntiles; ++tile) step(tile);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no direct load of this pass in flight
     __syncthreads();
@@ -507,6 +524,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     l_run = 0.0f;
     overflow = false;
     __syncthreads();
+    for (int tile = 0; tile < min(ntiles, kStages - 1); ++tile) gather(tile);
   }
 
   // (m, l) of head 16wv + j: every lane group holds the same m; l is summed
