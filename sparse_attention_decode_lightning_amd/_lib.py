@@ -55,7 +55,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with "
-            "`python -m sparse_attention_decode_lightning_amd.build` (needs ROCm hipcc)")
+            "`python sparse_attention_decode_lightning_amd/build.py` (needs ROCm hipcc)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ, F = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
                           ctypes.c_float)

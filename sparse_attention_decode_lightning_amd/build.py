@@ -1,6 +1,6 @@
 """Build libdsa.so (the C-ABI library) in-tree with hipcc for gfx950.
 
-    python -m sparse_attention_decode_lightning_amd.build
+    python sparse_attention_decode_lightning_amd/build.py
 
 Sources are compiled in parallel into ``_build/`` at the repository root and
 linked into ``sparse_attention_decode_lightning_amd/libdsa.so``.
