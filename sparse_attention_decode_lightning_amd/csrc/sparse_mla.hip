@@ -550,14 +550,13 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
       lse[(int64_t)row * kH + tid] = l > 0.0f ? m * kLn2 + logf(l) : -INFINITY;
     }
   } else {
+    // the split's accumulators in register order: value (nt, r) of lane l
+    // of wave wv at float4 (wv * 32 + nt) * 64 + l, so that every store
+    // instruction writes 1 KB of whole cache lines
     const int64_t part = (int64_t)row * n_splits + split;
+    f32x4_t *op = reinterpret_cast<f32x4_t *>(ws_acc + part * kH * kDL) + wv * 32 * kWave + lane;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int head = 16 * wv + 4 * g + r;
-      float *op = ws_acc + (part * kH + head) * kDL + j;
-#pragma unroll
-      for (int nt = 0; nt < 32; ++nt) op[16 * nt] = o[nt][r];
-    }
+    for (int nt = 0; nt < 32; ++nt) op[nt * kWave] = o[nt];
     if (tid < kH) {
       ws_ml[(part * kH + tid) * 2 + 0] = s_ml[tid][0];
       ws_ml[(part * kH + tid) * 2 + 1] = s_ml[tid][1];
@@ -565,59 +564,80 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
   }
 }
 
-// Merge the splits of one row: 256 threads = 4 heads x 64 threads x 8 dims.
-// O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, lse = M ln 2 + ln(sum ...).
-// One pass: splits are taken eight at a time with every load of the eight
-// issued before any is used, and the running sums move to each chunk's new
-// maximum (one round trip for up to eight splits).
-__global__ __launch_bounds__(256) void mla_combine_kernel(int n_splits,
-                                                          const float *__restrict__ ws_acc,
-                                                          const float *__restrict__ ws_ml,
-                                                          float *__restrict__ out,
-                                                          float *__restrict__ lse) {
+// Merge the splits of one row. The accumulators of a split are stored in the
+// main kernel's register order: float4 f = (wv * 32 + nt) * 64 + 16 g + j
+// holds heads 16 wv + 4 g + (0..3) at dim 16 nt + j. Thread (row, f) with
+// nt < 16 reads float4 f and f + 1024 (dim tile nt + 16, same heads) of every
+// split, whole lines, with the (m, l) pairs of its four heads, and merges:
+// O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, lse = M ln 2 +
+// ln(sum ...). Splits are taken eight at a time with every load of the eight
+// issued before any is used; the running sums move to each chunk's maximum.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineBlocksPerRow = kH * kDL / 8 / kCombineThreads;  // 16
+
+__global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(
+    int n_splits, const float *__restrict__ ws_acc, const float *__restrict__ ws_ml,
+    float *__restrict__ out, float *__restrict__ lse) {
   constexpr int kU = 8;
-  const int row = blockIdx.x / (kH / 4);
-  const int head = (blockIdx.x % (kH / 4)) * 4 + (threadIdx.x >> 6);
-  const int d0 = (threadIdx.x & 63) * 8;
-  const float *ml = ws_ml + ((int64_t)row * n_splits * kH + head) * 2;  // split s at + s*kH*2
-  const float *acc = ws_acc + (((int64_t)row * n_splits * kH + head) * kDL + d0);  // + s*kH*kDL
-  float M = -INFINITY, Lsum = 0.0f;
+  const int row = blockIdx.x / kCombineBlocksPerRow;
+  const int i = (blockIdx.x % kCombineBlocksPerRow) * kCombineThreads + threadIdx.x;  // < 4096
+  const int wv = i >> 10, nt = (i >> 6) & 15, l = i & 63;
+  const int head0 = 16 * wv + 4 * (l >> 4), dim = 16 * nt + (l & 15);
+  const int64_t split_f4 = kH * kDL / 4;
+  const f32x4_t *acc = reinterpret_cast<const f32x4_t *>(ws_acc) +
+                       (int64_t)row * n_splits * split_f4 + (wv * 32 + nt) * kWave + l;
+  const f32x4_t *ml = reinterpret_cast<const f32x4_t *>(ws_ml) +
+                      ((int64_t)row * n_splits * kH + head0) / 2;  // + s * kH / 2
+  float M[4], Lsum[4];
   f32x4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    M[r] = -INFINITY;
+    Lsum[r] = 0.0f;
+  }
   for (int s0 = 0; s0 < n_splits; s0 += kU) {
-    float m[kU], l[kU];
-    f32x4_t x0[kU], x1[kU];
+    f32x4_t x0[kU], x1[kU], p0[kU], p1[kU];  // p0 = (m, l) of heads 0, 1; p1 of heads 2, 3
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const bool in = s0 + u < n_splits;
-      const float *src = acc + (int64_t)(s0 + u) * kH * kDL;
-      m[u] = in ? ml[(s0 + u) * kH * 2] : -INFINITY;
-      l[u] = in ? ml[(s0 + u) * kH * 2 + 1] : 0.0f;
-      x0[u] = in ? *reinterpret_cast<const f32x4_t *>(src) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      x1[u] = in ? *reinterpret_cast<const f32x4_t *>(src + 4) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      const int64_t so = (int64_t)(s0 + u);
+      x0[u] = in ? acc[so * split_f4] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      x1[u] = in ? acc[so * split_f4 + 16 * kWave] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      p0[u] = in ? ml[so * (kH / 2)] : f32x4_t{-INFINITY, 0.0f, -INFINITY, 0.0f};
+      p1[u] = in ? ml[so * (kH / 2) + 1] : f32x4_t{-INFINITY, 0.0f, -INFINITY, 0.0f};
     }
-    float Mc = M;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) Mc = fmaxf(Mc, m[u]);
-    if (Mc == -INFINITY) continue;  // nothing valid yet
-    const float rescale = exp2f(M - Mc);  // 0 while M is -inf
-    Lsum *= rescale;
-    a0 *= rescale;
-    a1 *= rescale;
+    for (int r = 0; r < 4; ++r) {
+      auto m_of = [&](int u) { return r < 2 ? p0[u][2 * r] : p1[u][2 * r - 4]; };
+      auto l_of = [&](int u) { return r < 2 ? p0[u][2 * r + 1] : p1[u][2 * r - 3]; };
+      float Mc = M[r];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const float wgt = exp2f(m[u] - Mc);
-      Lsum += wgt * l[u];
-      a0 += wgt * x0[u];
-      a1 += wgt * x1[u];
+      for (int u = 0; u < kU; ++u) Mc = fmaxf(Mc, m_of(u));
+      if (Mc == -INFINITY) continue;  // nothing valid yet
+      const float rescale = exp2f(M[r] - Mc);  // 0 while M is -inf
+      float ls = Lsum[r] * rescale, s0v = a0[r] * rescale, s1v = a1[r] * rescale;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const float wgt = exp2f(m_of(u) - Mc);
+        ls += wgt * l_of(u);
+        s0v += wgt * x0[u][r];
+        s1v += wgt * x1[u][r];
+      }
+      M[r] = Mc;
+      Lsum[r] = ls;
+      a0[r] = s0v;
+      a1[r] = s1v;
     }
-    M = Mc;
   }
-  const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
-  float *dst = out + (((int64_t)row * kH + head) * kDL + d0);
-  *reinterpret_cast<f32x4_t *>(dst) = a0 * inv;
-  *reinterpret_cast<f32x4_t *>(dst + 4) = a1 * inv;
-  if (lse != nullptr && (threadIdx.x & 63) == 0)
-    lse[(int64_t)row * kH + head] = Lsum > 0.0f ? M * kLn2 + logf(Lsum) : -INFINITY;
+  float *dst = out + ((int64_t)row * kH + head0) * kDL + dim;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float inv = Lsum[r] > 0.0f ? 1.0f / Lsum[r] : 0.0f;
+    dst[r * kDL] = a0[r] * inv;
+    dst[r * kDL + 256] = a1[r] * inv;
+    if (lse != nullptr && nt == 0 && (l & 15) == 0)
+      lse[(int64_t)row * kH + head0 + r] = Lsum[r] > 0.0f ? M[r] * kLn2 + logf(Lsum[r]) : -INFINITY;
+  }
 }
 
 // Any head count, widths and element type: one 256-thread workgroup per
@@ -730,7 +750,8 @@ hipError_t launch_sparse_mla(const BatchArgs &bt, const void *q, int32_t q_dtype
                        lse, ws_acc, ws_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
-    hipLaunchKernelGGL(mla_combine_kernel, dim3(bt.total_q * (n_heads / 4)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(mla_combine_kernel, dim3(bt.total_q * kCombineBlocksPerRow),
+                       dim3(kCombineThreads), 0, stream,
                        S, ws_acc, ws_ml, out, lse);
     return hipGetLastError();
   }
