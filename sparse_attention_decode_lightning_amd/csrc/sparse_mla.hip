@@ -303,11 +303,15 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     goff[n] = (uint32_t)(16 * chunk_swz(lc, 8 * wv + rl)) + kBias - 1024u * (n % 4);
   }
   const uint8_t *kv_base = kv - kBias;
-  auto gather = [&](int tile) {
+  // row ids of this wave's eight rows of a tile (read one tile ahead of the
+  // copy that needs them, so the copy never waits on this LDS read)
+  auto rowids = [&](int tile, u32x4_t &ra, u32x4_t &rb) {
+    ra = *reinterpret_cast<const u32x4_t *>(s_rowid + tile * kTileN + 8 * wv);
+    rb = *reinterpret_cast<const u32x4_t *>(s_rowid + tile * kTileN + 8 * wv + 4);
+  };
+  auto gather = [&](int tile, const u32x4_t ra, const u32x4_t rb) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         lds_tiles + (uint32_t)(tile & (kStages - 1)) * kTileBytes + 8 * wv * kRowBytes);
-    const u32x4_t ra = *reinterpret_cast<const u32x4_t *>(s_rowid + tile * kTileN + 8 * wv);
-    const u32x4_t rb = *reinterpret_cast<const u32x4_t *>(s_rowid + tile * kTileN + 8 * wv + 4);
     const uint32_t rid[8] = {ra.x & ~kInvalid, ra.y & ~kInvalid, ra.z & ~kInvalid, ra.w & ~kInvalid,
                              rb.x & ~kInvalid, rb.y & ~kInvalid, rb.z & ~kInvalid, rb.w & ~kInvalid};
     if constexpr (kOff32) {
@@ -375,6 +379,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
   __builtin_amdgcn_s_waitcnt(0x0070);
   __syncthreads();  // row table visible
 
+  u32x4_t ra_n, rb_n;  // row ids of the next tile to copy
   auto step = [&](int tile) {
     // this wave's loads of `tile` have landed (later tiles may be in flight)
     const int ahead = min(ntiles - 1 - tile, kStages - 2);
@@ -389,7 +394,8 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     // every wave is done with the stage of tile - 1.
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if (tile + kStages - 1 < ntiles) gather(tile + kStages - 1);
+    if (tile + kStages - 1 < ntiles) gather(tile + kStages - 1, ra_n, rb_n);
+    rowids(min(tile + kStages, ntiles - 1), ra_n, rb_n);
 
     // (a fully masked tile is computed like any other: its logits are all
     // -inf and add nothing)
@@ -511,7 +517,14 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
   // one is at most 2^kHeadroom), then the split is walked again from the
   // raised references. Not leaving the tile loop early keeps the
   // accumulators in the registers the MFMAs write.
-  for (int tile = 0; tile < min(ntiles, kStages - 1); ++tile) gather(tile);
+  auto first_gathers = [&]() {
+    for (int tile = 0; tile < min(ntiles, kStages - 1); ++tile) {
+      rowids(tile, ra_n, rb_n);
+      gather(tile, ra_n, rb_n);
+    }
+    rowids(max(min(kStages - 1, ntiles - 1), 0), ra_n, rb_n);
+  };
+  first_gathers();
   for (;;) {
     for (int tile = 0; tile < ntiles; ++tile) step(tile);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no direct load of this pass in flight
@@ -524,7 +537,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     l_run = 0.0f;
     overflow = false;
     __syncthreads();
-    for (int tile = 0; tile < min(ntiles, kStages - 1); ++tile) gather(tile);
+    first_gathers();
   }
 
   // (m, l) of head 16wv + j: every lane group holds the same m; l is summed
