@@ -226,6 +226,63 @@ def traffic_summary(fetch_dir: str, write_dir: str, workload: str, calls_per_sta
 
 
 # --------------------------------------------------------------------------
+# the cache append that precedes the path (measured on its own, not in `value`)
+# --------------------------------------------------------------------------
+
+
+def time_kv_append(dsa, inp, wl, kvs, keys, stream, flush, args, reps=10):
+    """Append one new token per query row (its own position t_r) to every layer's latent
+    cache and to the indexer-key cache; HIP events around each append after a cache
+    eviction. Runs after the timed steps: it overwrites those rows of the caches."""
+    dev = inp.block_table.device
+    bt = inp.block_table.cpu().numpy()
+    P = wl.page_size
+    slots = []
+    for b, (L, q) in enumerate(zip(inp.seq_lens_host, inp.q_lens_host)):
+        for i in range(q):
+            t = L - q + i
+            slots.append(int(bt[b, t // P]) * P + t % P)
+    T = len(slots)
+    slot_t = torch.tensor(slots, dtype=torch.int32, device=dev)
+    g = torch.Generator(device=dev).manual_seed(11)
+    row = wl.d_latent + wl.d_rope
+    lat_dt = torch.bfloat16 if wl.mla_dtype == "bf16" else torch.float32
+    key_src_dt = torch.float32 if wl.idx_k_dtype == "f32" else torch.bfloat16
+    lat_new = [torch.randn((T, row), generator=g, device=dev).to(lat_dt) for _ in kvs]
+    key_new = torch.randn((T, wl.idx_dim), generator=g, device=dev).to(key_src_dt)
+
+    def append():
+        for l, kv in enumerate(kvs):
+            if l == 0:
+                dsa.kv_append(slot_t, lat_new[0], kv, key_new, keys)
+            else:
+                dsa.kv_append(slot_t, lat_new[l], kv)
+
+    append()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        if not args.no_flush:
+            flush.sum()
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        append()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b_))
+    ms = float(np.median(ts))
+    e = 2 if wl.mla_dtype == "bf16" else 4
+    key_in = wl.idx_dim * (4 if wl.idx_k_dtype == "f32" else 2)
+    key_out = {"bf16": 2 * wl.idx_dim, "f32": 4 * wl.idx_dim, "fp8": wl.idx_dim + 4}[wl.idx_k_dtype]
+    per_token = len(kvs) * (2 * row * e) + key_in + key_out + 4 * len(kvs)
+    return {"tokens": T, "calls": len(kvs), "us": ms * 1e3, "bytes": T * per_token,
+            "gbs": T * per_token / (ms * 1e-3) / 1e9,
+            "note": "one new token per query row into every layer's latent cache and the "
+                    "indexer-key cache (fp8 keys quantised per token); median of "
+                    f"{reps} evicted runs; not part of value"}
+
+
+# --------------------------------------------------------------------------
 
 
 def main():
@@ -391,6 +448,7 @@ def main():
                          algorithmic_bytes_per_launch=d_bytes, avg_launch_ms=d_ms),
         "wall_s_timed_loop": wall,
     }
+    line["kv_append"] = time_kv_append(dsa, inp, wl, kvs, keys, stream, flush, args)
     if args.copy_probe:
         src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

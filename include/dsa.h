@@ -209,6 +209,49 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_d
                               float scale, float *out, float *lse, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/*
+ * Append this step's new tokens to the paged caches, the write that precedes
+ * selection ("GLM-5.2 on vLLM Ascend: Request-to-Backend Inference Path",
+ * section "8. The SFA backend, step by step", "Write paged cache": the slot
+ * mapping scatters the new latent KV and, for layers that own an indexer, the
+ * new indexer keys and scales into their physical pages; "Making GLM-5.2
+ * Sparse on TPUs", section "Append new KV without moving the resident
+ * cache": only the new rows are written, the resident ones stay intact).
+ *
+ * Token i goes to physical slot slot_mapping[i] = page * page_size + offset
+ * of every cache given. A negative slot, or one at or past num_pages *
+ * page_size, skips the token. No other byte of either cache is written. When
+ * two tokens map to one slot, which of them lands is unspecified.
+ *
+ *   slot_mapping  device [n_tokens] int32
+ *   latent        device [n_tokens, kv->row_elems] of kv->dtype (F32 or BF16),
+ *                 copied into the latent cache; NULL together with kv = NULL
+ *   kv            paged latent cache, written in place (the call writes through
+ *                 its `data` pointer)
+ *   idx_keys      device [n_tokens, k_idx->row_elems] of key_dtype (F32 or
+ *                 BF16), finite; NULL together with k_idx = NULL
+ *   k_idx         paged indexer-key cache, written in place (data, and scale
+ *                 for fp8). An F32 or BF16 cache takes a copy of the row and
+ *                 needs key_dtype equal to its dtype. An FP8_E4M3 cache takes
+ *                 the row quantised per token: sigma = max_d |k[d]| / 448 in
+ *                 fp32 (sigma = 1 for an all-zero row), byte[d] = the e4m3
+ *                 value nearest to clamp(k[d] / sigma, -448, 448), ties to the
+ *                 even code, and scale[slot] = sigma, so that sigma *
+ *                 e4m3(byte) is the stored key.
+ *
+ * With n_tokens = 0 nothing is enqueued and the row and slot arrays may be
+ * NULL.
+ *
+ * Errors: DSA_ERR_NULL (both caches NULL; with n_tokens > 0, a cache without
+ * its source rows or the reverse, or a NULL slot_mapping; NULL cache data or
+ * fp8 scale), DSA_ERR_SHAPE (n_tokens < 0, bad cache geometry, misaligned
+ * pointers), DSA_ERR_DTYPE (an fp8 latent cache, a key type that does not fit
+ * the cache), DSA_ERR_LAUNCH.
+ */
+dsa_status dsa_kv_append(const int32_t *slot_mapping, int32_t n_tokens, const void *latent,
+                         const dsa_paged_cache *kv, const void *idx_keys, int32_t key_dtype,
+                         const dsa_paged_cache *k_idx, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

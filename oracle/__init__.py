@@ -8,11 +8,14 @@ from . import dsa_oracle  # noqa: F401
 from .dsa_oracle import (  # noqa: F401
     bf16_to_f64,
     decode,
+    e4m3fn_encode,
     e4m3fn_table,
     glm52_indexer_pattern,
     indexer_owner_layers,
     indexer_scores,
     indexer_scores_row,
+    kv_append,
+    quantize_key_e4m3,
     row_positions,
     run,
     sparse_mla,

@@ -290,3 +290,88 @@ def glm52_indexer_pattern(n_layers: int = 78) -> str:
     """
     full = {0, 1, 2} | set(range(6, 75, 4))
     return "".join("F" if i in full else "S" for i in range(n_layers))
+
+
+# --------------------------------------------------------------------------
+# appending new tokens to the paged caches
+# --------------------------------------------------------------------------
+
+
+def e4m3fn_encode(x: np.ndarray) -> np.ndarray:
+    """Finite float32 values in [-448, 448] -> OCP E4M3FN codes (uint8).
+
+    The code whose value is nearest to x, among the finite codes of x's sign;
+    at an exact midpoint between two codes the one with an even code (mantissa
+    bit 0 clear) wins. +0 and -0 keep their sign. Found by comparing x with
+    every finite code value of the decode table, not by bit manipulation.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    flat = x.reshape(-1).astype(np.float64)
+    mags = _E4M3[:0x7F]  # codes 0x00..0x7E: every finite non-negative value
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for i, v in enumerate(flat):
+        if not (abs(v) <= 448.0):
+            raise ValueError("e4m3fn_encode takes finite values in [-448, 448]")
+        neg = math.copysign(1.0, v) < 0
+        d = np.abs(mags - abs(v))
+        near = np.flatnonzero(d == d.min())
+        code = int(near[0]) if len(near) == 1 else int(next(c for c in near if c % 2 == 0))
+        out[i] = code | (0x80 if neg else 0)
+    return out.reshape(x.shape)
+
+
+def quantize_key_e4m3(k: np.ndarray):
+    """One token's indexer key -> (e4m3fn codes, fp32 scale).
+
+    sigma = max|k| / 448 in fp32 (1 for an all-zero key), codes = nearest
+    e4m3fn values of clamp(k / sigma, -448, 448) computed in fp32, so that
+    sigma * e4m3(code) is the stored key ("GLM-5.2 on vLLM Ascend ...",
+    section "7. GLM-5.2 shared-indexer construction": FP8 e4m3 keys with FP32
+    scales). The quantised code is an integer decided by floating point, so
+    this step uses the stored format's fp32 arithmetic, not float64.
+    """
+    k = np.asarray(k, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(k))) if k.size else np.float32(0.0)
+    sigma = amax / np.float32(448.0) if amax > 0 else np.float32(1.0)
+    q = np.clip(k / sigma, np.float32(-448.0), np.float32(448.0)).astype(np.float32)
+    return e4m3fn_encode(q), np.float32(sigma)
+
+
+def kv_append(slot_mapping, latent=None, kv_cache=None, idx_keys=None, key_cache=None,
+              key_scale=None, key_cache_dtype: str = "bf16"):
+    """Write new tokens into paged caches; returns updated copies (inputs untouched).
+
+    ("GLM-5.2 on vLLM Ascend ...", section "8. The SFA backend, step by step",
+    "Write paged cache": the slot mapping scatters new latent rows and indexer
+    keys/scales into their physical pages; "Making GLM-5.2 Sparse on TPUs",
+    section "Append new KV without moving the resident cache".)
+
+    Caches are raw storage arrays [num_pages, page_size, row]: uint16 for bf16,
+    float32 for f32, uint8 for fp8 (with key_scale [num_pages, page_size]).
+    Token i lands in slot s = slot_mapping[i] (page s // page_size, offset
+    s % page_size); a negative slot or one past the pool skips the token. A
+    latent row, or a key row for an f32/bf16 key cache, is stored as given (its
+    raw elements); a key row for an fp8 cache is quantised by
+    quantize_key_e4m3 from its float32 value.
+    """
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    kv_out = None if kv_cache is None else np.array(kv_cache, copy=True)
+    key_out = None if key_cache is None else np.array(key_cache, copy=True)
+    scale_out = None if key_scale is None else np.array(key_scale, copy=True)
+    for i, s in enumerate(slots):
+        if kv_out is not None:
+            n_pages, P = kv_out.shape[:2]
+            if 0 <= s < n_pages * P:
+                kv_out[s // P, s % P] = np.asarray(latent)[i]
+        if key_out is not None:
+            n_pages, P = key_out.shape[:2]
+            if 0 <= s < n_pages * P:
+                row = np.asarray(idx_keys)[i]
+                if key_cache_dtype == "fp8":
+                    vals = row if row.dtype == np.float32 else bf16_to_f64(row).astype(np.float32)
+                    codes, sigma = quantize_key_e4m3(vals)
+                    key_out[s // P, s % P] = codes
+                    scale_out[s // P, s % P] = sigma
+                else:
+                    key_out[s // P, s % P] = row
+    return kv_out, key_out, scale_out

@@ -29,7 +29,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "Batch", "PagedCache", "DSAError", "indexer_scores", "topk", "sparse_mla_fwd",
-    "topk_workspace_size", "sparse_mla_workspace_size", "abi_version",
+    "topk_workspace_size", "sparse_mla_workspace_size", "abi_version", "kv_append",
 ]
 
 _DT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.uint8: DSA_FP8_E4M3,
@@ -177,3 +177,38 @@ def sparse_mla_fwd(batch: Batch, q: torch.Tensor, kv: PagedCache, indices: torch
                                  0 if lse is None else _dev(lse, "lse", torch.float32), wp, wb,
                                  _stream(q.device)), "dsa_sparse_mla_fwd")
     return out, lse
+
+
+def kv_append(slot_mapping: torch.Tensor, latent: Optional[torch.Tensor] = None,
+              kv: Optional[PagedCache] = None, idx_keys: Optional[torch.Tensor] = None,
+              k_idx: Optional[PagedCache] = None) -> None:
+    """Write new tokens into paged caches in place: token i to slot slot_mapping[i]
+    (page * page_size + offset; negative or out-of-pool slots are skipped). Latent
+    rows are copied; indexer keys are copied, or quantised per token for an e4m3
+    cache (scale = max|k| / 448)."""
+    n = int(slot_mapping.numel())
+    if (latent is None) != (kv is None) or (idx_keys is None) != (k_idx is None):
+        raise ValueError("each cache needs its new rows and each set of rows its cache")
+    sp = _dev(slot_mapping, "slot_mapping", torch.int32)
+    lp, kp, kd = 0, 0, DSA_BF16
+    kvc = ctypes.POINTER(DsaPagedCache)()
+    kic = ctypes.POINTER(DsaPagedCache)()
+    if kv is not None:
+        if latent.dim() != 2 or latent.shape[0] != n or latent.shape[1] != kv.data.shape[2]:
+            raise ValueError("latent must be [n_tokens, row_elems]")
+        if latent.dtype != kv.data.dtype:
+            raise TypeError("latent rows must have the latent cache's dtype")
+        lp = _dev(latent, "latent")
+        kvs = kv.c()
+        kvc = ctypes.pointer(kvs)
+    if k_idx is not None:
+        if idx_keys.dim() != 2 or idx_keys.shape[0] != n or idx_keys.shape[1] != k_idx.data.shape[2]:
+            raise ValueError("idx_keys must be [n_tokens, row_elems]")
+        kd = _DT.get(idx_keys.dtype)
+        if kd not in (DSA_F32, DSA_BF16):
+            raise TypeError("idx_keys must be float32 or bfloat16")
+        kp = _dev(idx_keys, "idx_keys")
+        kis = k_idx.c()
+        kic = ctypes.pointer(kis)
+    dev = slot_mapping.device
+    check(lib.dsa_kv_append(sp, n, lp, kvc, kp, kd, kic, _stream(dev)), "dsa_kv_append")

@@ -39,15 +39,14 @@ dsa_status check_batch(const dsa_batch *bt, BatchArgs *out) {
   return DSA_OK;
 }
 
-dsa_status check_cache(const dsa_paged_cache *c, const BatchArgs &bt, CacheArgs *out) {
-  if (c == nullptr || c->data == nullptr) return DSA_ERR_NULL;
+// Element type, geometry and alignment of a paged cache.
+dsa_status check_cache_geometry(const dsa_paged_cache *c, CacheArgs *out) {
+  if (c->data == nullptr) return DSA_ERR_NULL;
   if (c->dtype != DSA_F32 && c->dtype != DSA_BF16 && c->dtype != DSA_FP8_E4M3)
     return DSA_ERR_DTYPE;
   if (c->dtype == DSA_FP8_E4M3 && c->scale == nullptr) return DSA_ERR_NULL;
   if (c->num_pages < 1 || c->page_size < 1 || c->row_elems < 1) return DSA_ERR_SHAPE;
   if (!aligned(c->data, 16) || (c->dtype == DSA_FP8_E4M3 && !aligned(c->scale, 4)))
-    return DSA_ERR_SHAPE;
-  if (bt.total_q > 0 && (int64_t)bt.bt_stride < ceil_div(bt.max_seq_len, c->page_size))
     return DSA_ERR_SHAPE;
   out->data = c->data;
   out->scale = c->dtype == DSA_FP8_E4M3 ? c->scale : nullptr;
@@ -55,6 +54,16 @@ dsa_status check_cache(const dsa_paged_cache *c, const BatchArgs &bt, CacheArgs 
   out->page_size = c->page_size;
   out->row_elems = c->row_elems;
   out->dtype = c->dtype;
+  return DSA_OK;
+}
+
+// A cache read through a batch's block table: its pages must cover max_seq_len.
+dsa_status check_cache(const dsa_paged_cache *c, const BatchArgs &bt, CacheArgs *out) {
+  if (c == nullptr) return DSA_ERR_NULL;
+  const dsa_status st = check_cache_geometry(c, out);
+  if (st != DSA_OK) return st;
+  if (bt.total_q > 0 && (int64_t)bt.bt_stride < ceil_div(bt.max_seq_len, c->page_size))
+    return DSA_ERR_SHAPE;
   return DSA_OK;
 }
 
@@ -156,6 +165,40 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_d
   return launch_status(dsa::launch_sparse_mla(bt, q, q_dtype, n_heads, d_latent, d_rope, kc,
                                               indices, k, scale, out, lse, workspace,
                                               workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+dsa_status dsa_kv_append(const int32_t *slot_mapping, int32_t n_tokens, const void *latent,
+                         const dsa_paged_cache *kv, const void *idx_keys, int32_t key_dtype,
+                         const dsa_paged_cache *k_idx, void *stream) {
+  if (n_tokens < 0) return DSA_ERR_SHAPE;
+  if (kv == nullptr && k_idx == nullptr) return DSA_ERR_NULL;
+  // with no tokens the row and slot arrays may be empty (NULL)
+  if (n_tokens > 0 && ((kv == nullptr) != (latent == nullptr) ||
+                       (k_idx == nullptr) != (idx_keys == nullptr) || slot_mapping == nullptr))
+    return DSA_ERR_NULL;
+  if (slot_mapping != nullptr && !aligned(slot_mapping, 4)) return DSA_ERR_SHAPE;
+  CacheArgs kc, ic;
+  if (kv != nullptr) {
+    const dsa_status st = check_cache_geometry(kv, &kc);
+    if (st != DSA_OK) return st;
+    if (kc.dtype == DSA_FP8_E4M3) return DSA_ERR_DTYPE;
+    if (latent != nullptr && !aligned(latent, kc.dtype == DSA_F32 ? 4 : 2)) return DSA_ERR_SHAPE;
+  }
+  if (k_idx != nullptr) {
+    const dsa_status st = check_cache_geometry(k_idx, &ic);
+    if (st != DSA_OK) return st;
+    if (key_dtype != DSA_F32 && key_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (ic.dtype != DSA_FP8_E4M3 && ic.dtype != key_dtype) return DSA_ERR_DTYPE;
+    if (idx_keys != nullptr && !aligned(idx_keys, key_dtype == DSA_F32 ? 4 : 2))
+      return DSA_ERR_SHAPE;
+  }
+  if (n_tokens == 0) return DSA_OK;
+  // one wave per (token, cache): the grid must fit
+  if ((int64_t)n_tokens * 2 > (int64_t)0x7FFFFFFF) return DSA_ERR_SHAPE;
+  return launch_status(dsa::launch_kv_append(slot_mapping, n_tokens, latent,
+                                             kv != nullptr ? &kc : nullptr, idx_keys, key_dtype,
+                                             k_idx != nullptr ? &ic : nullptr,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -48,4 +48,8 @@ hipError_t launch_sparse_mla(const BatchArgs &bt, const void *q, int32_t q_dtype
                              const int32_t *indices, int32_t k, float scale, float *out, float *lse,
                              void *workspace, size_t ws_bytes, hipStream_t stream);
 
+hipError_t launch_kv_append(const int32_t *slots, int32_t n_tokens, const void *latent,
+                            const CacheArgs *kv, const void *keys, int32_t key_dtype,
+                            const CacheArgs *kidx, hipStream_t stream);
+
 }  // namespace dsa

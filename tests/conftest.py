@@ -20,8 +20,14 @@ def golden_dir():
 def _ensure_built():
     lib = os.path.join(ROOT, "sparse_attention_decode_lightning_amd", "libdsa.so")
     if not os.path.exists(lib):
-        from sparse_attention_decode_lightning_amd import build as _b
-        _b.build(verbose=False)
+        # load the build script by path: importing the package needs the library
+        import importlib.util
+
+        path = os.path.join(ROOT, "sparse_attention_decode_lightning_amd", "build.py")
+        spec = importlib.util.spec_from_file_location("_dsa_build", path)
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
+        b.build(verbose=False)
 
 
 _ensure_built()

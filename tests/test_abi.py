@@ -140,3 +140,33 @@ def test_workspace_sizes_are_pure_functions_of_bounds():
     assert s > 0 and s == L.lib.dsa_sparse_mla_workspace_size(32, 64, 512, 2048)
     assert L.lib.dsa_sparse_mla_workspace_size(4096, 64, 512, 2048) == 0
     assert L.lib.dsa_sparse_mla_workspace_size(0, 64, 512, 2048) == 0
+
+
+def _append(slots=FAKE, n=4, lat=FAKE, kv=None, keys=FAKE, kd=L.DSA_BF16, kc=None):
+    kv = _cache(row_elems=576) if kv is None else kv
+    kc = _cache(dtype=L.DSA_FP8_E4M3) if kc is None else kc
+    return L.lib.dsa_kv_append(slots, n, lat, ctypes.byref(kv) if kv is not False else None,
+                               keys, kd, ctypes.byref(kc) if kc is not False else None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), 2),
+    (dict(kv=False, kc=False, lat=0, keys=0), 1),
+    (dict(lat=0), 1),                                    # latent cache without rows
+    (dict(kv=False), 1),                                 # rows without a latent cache
+    (dict(keys=0), 1),
+    (dict(slots=0), 1),
+    (dict(slots=FAKE + 2), 2),                           # misaligned slot mapping
+    (dict(kd=L.DSA_FP8_E4M3), 3),                        # keys must arrive as f32 or bf16
+    (dict(kc=_cache(dtype=L.DSA_F32), kd=L.DSA_BF16), 3),  # copy needs the cache's type
+    (dict(kv=_cache(row_elems=576, dtype=L.DSA_FP8_E4M3)), 3),  # no fp8 latent cache
+    (dict(kc=_cache(dtype=L.DSA_FP8_E4M3, scale=0)), 1),
+    (dict(kv=_cache(row_elems=576, data=FAKE + 8)), 2),
+    (dict(kv=_cache(row_elems=576, page_size=0)), 2),
+])
+def test_kv_append_rejects_bad_arguments(kw, code):
+    assert _append(**kw) == code
+
+
+def test_kv_append_empty_is_a_no_op():
+    assert _append(n=0, slots=0, lat=0, keys=0) == 0

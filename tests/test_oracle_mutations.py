@@ -81,7 +81,46 @@ def _e4m3_fnuz(codes):
     return tab[np.asarray(codes, dtype=np.uint8)]
 
 
+def _e4m3_ties_away(x):
+    # round half away from zero instead of to the even code
+    x = np.asarray(x, dtype=np.float32)
+    tab = O.e4m3fn_table()[:0x7F]
+    flat = x.reshape(-1).astype(np.float64)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for i, v in enumerate(flat):
+        d = np.abs(tab - abs(v))
+        out[i] = int(np.flatnonzero(d == d.min())[-1]) | (0x80 if np.signbit(v) else 0)
+    return out.reshape(x.shape)
+
+
+def _e4m3_truncate(x):
+    # round toward zero
+    x = np.asarray(x, dtype=np.float32)
+    tab = O.e4m3fn_table()[:0x7F]
+    flat = x.reshape(-1).astype(np.float64)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for i, v in enumerate(flat):
+        out[i] = int(np.flatnonzero(tab <= abs(v))[-1]) | (0x80 if np.signbit(v) else 0)
+    return out.reshape(x.shape)
+
+
+_orig_quant = O.quantize_key_e4m3
+
+
+def _scale_by_255(k):
+    # the scale of an int8-style format instead of e4m3's 448
+    k = np.asarray(k, dtype=np.float32)
+    sigma = np.float32(np.max(np.abs(k))) / np.float32(255.0)
+    return O.e4m3fn_encode(np.clip(k / sigma, -448, 448).astype(np.float32)), sigma
+
+
 MUTATIONS = [
+    ("e4m3fn_encode", _e4m3_ties_away, ["test_e4m3_encode_round_trip_and_ties_to_even",
+                                        "test_e4m3_encode_matches_torch_cast"]),
+    ("e4m3fn_encode", _e4m3_truncate, ["test_e4m3_encode_round_trip_and_ties_to_even",
+                                       "test_e4m3_encode_matches_torch_cast"]),
+    ("quantize_key_e4m3", _scale_by_255, ["test_quantize_key_scale_and_error_bound",
+                                          "test_quantize_key_matches_workload_recipe"]),
     ("indexer_scores_row", _no_relu, ["test_indexer_one_hot_keys_read_out_query_columns",
                                       "test_indexer_single_head_relu_of_dot"]),
     ("indexer_scores_row", _reversed_head_weights, ["test_indexer_one_hot_keys_read_out_query_columns"]),

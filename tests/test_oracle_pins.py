@@ -424,3 +424,98 @@ def test_indexshare_pattern_matches_printed_string(golden_dir):
 def test_indexshare_rejects_shared_layer_without_owner():
     with pytest.raises(ValueError):
         O.indexer_owner_layers("SFF")
+
+
+# --------------------------------------------------------------------------
+# paged append: e4m3 quantisation and the slot scatter
+# --------------------------------------------------------------------------
+
+
+def _e4m3_edge_values() -> np.ndarray:
+    """Every finite e4m3 value, every midpoint of two neighbours, and the floats beside them."""
+    tab = O.e4m3fn_table()
+    mags = np.sort(tab[:0x7F]).astype(np.float32)
+    mids = ((mags[:-1].astype(np.float64) + mags[1:]) / 2).astype(np.float32)  # exact in fp32
+    near = np.concatenate([np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(448))])
+    vals = np.concatenate([mags, mids, near, [2.0 ** -12, 2.0 ** -10, 1e-30, 447.99]])
+    return np.concatenate([vals, -vals, [0.0, -0.0]]).astype(np.float32)
+
+
+def test_e4m3_encode_matches_torch_cast():
+    """Library routine: torch's float8_e4m3fn conversion rounds to nearest, ties to even."""
+    rng = np.random.default_rng(7)
+    rand = rng.standard_normal(3000) * rng.choice([1e-3, 0.05, 1.0, 40.0, 300.0], 3000)
+    x = np.concatenate([_e4m3_edge_values(), np.clip(rand, -448, 448)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3fn_encode(x), ref)
+
+
+def test_e4m3_encode_round_trip_and_ties_to_even():
+    """Closed form: a code's own value encodes to it; a midpoint goes to the even code."""
+    tab = O.e4m3fn_table()
+    for c in range(256):
+        if not np.isnan(tab[c]):
+            v = np.float32(-0.0) if c == 0x80 else np.float32(tab[c])
+            assert int(O.e4m3fn_encode(v)) == c, hex(c)
+    for c in range(0x7E):  # neighbours c, c + 1 among the positive codes
+        mid = np.float32((tab[c] + tab[c + 1]) / 2)
+        want = c if c % 2 == 0 else c + 1
+        assert int(O.e4m3fn_encode(mid)) == want
+        assert int(O.e4m3fn_encode(-mid)) == want | 0x80
+
+
+def test_quantize_key_scale_and_error_bound():
+    """sigma = max|k| / 448 in fp32; the largest element lands on +-448; every element is
+    within half an e4m3 step (2^-4 relative, or sigma 2^-10 in the subnormal range)."""
+    rng = np.random.default_rng(8)
+    for _ in range(20):
+        k = (rng.standard_normal(128) * rng.choice([1e-3, 1.0, 50.0])).astype(np.float32)
+        codes, sigma = O.quantize_key_e4m3(k)
+        assert sigma == np.float32(np.abs(k).max()) / np.float32(448.0)
+        assert int(codes[np.argmax(np.abs(k))]) & 0x7F == 0x7E
+        deq = np.float64(sigma) * O.e4m3fn_table()[codes]
+        bound = np.maximum(np.abs(k) * 2.0 ** -4, float(sigma) * 2.0 ** -10) * (1 + 1e-6)
+        assert np.all(np.abs(deq - k) <= bound)
+    z, s0 = O.quantize_key_e4m3(np.zeros(128, np.float32))
+    assert s0 == np.float32(1.0) and not z.any()
+
+
+def test_quantize_key_matches_workload_recipe():
+    """The workload generator's torch recipe (amax / 448, clamp, float8 cast) and the oracle
+    give the same bytes and scales."""
+    g = torch.Generator().manual_seed(9)
+    k = torch.randn((64, 128), generator=g) * torch.rand((64, 1), generator=g) * 10
+    sig = k.abs().amax(dim=-1) / 448.0
+    ref = (k / sig[:, None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for i in range(64):
+        codes, sigma = O.quantize_key_e4m3(k[i].numpy())
+        assert sigma == np.float32(sig[i].item())
+        assert np.array_equal(codes, ref[i])
+
+
+def test_kv_append_writes_only_mapped_slots():
+    """Invariant: mapped slots take the new rows, skipped tokens (negative or out-of-pool
+    slots) and every other slot keep their bytes; fp8 keys carry their scale."""
+    rng = np.random.default_rng(10)
+    pages, P, R, D = 5, 4, 12, 8
+    kv = rng.integers(0, 1 << 15, (pages, P, R), dtype=np.uint16)
+    keys = rng.integers(0, 0x7F, (pages, P, D), dtype=np.uint8)
+    scale = rng.random((pages, P)).astype(np.float32)
+    slots = np.array([7, -1, pages * P, 0, 19, -3], dtype=np.int32)
+    lat = rng.integers(0, 1 << 15, (6, R), dtype=np.uint16)
+    new_k = rng.standard_normal((6, D)).astype(np.float32)
+    kv2, keys2, scale2 = O.kv_append(slots, lat, kv, new_k, keys, scale, key_cache_dtype="fp8")
+    written = {7: 0, 0: 3, 19: 4}
+    for s in range(pages * P):
+        p, o = divmod(s, P)
+        if s in written:
+            i = written[s]
+            assert np.array_equal(kv2[p, o], lat[i])
+            codes, sigma = O.quantize_key_e4m3(new_k[i])
+            assert np.array_equal(keys2[p, o], codes) and scale2[p, o] == sigma
+        else:
+            assert np.array_equal(kv2[p, o], kv[p, o])
+            assert np.array_equal(keys2[p, o], keys[p, o]) and scale2[p, o] == scale[p, o]
+    kv3, keys3, _ = O.kv_append(slots, lat, kv, new_k.astype(np.float32), keys, None,
+                                key_cache_dtype="f32")
+    assert keys3.dtype == keys.dtype and np.array_equal(kv3, kv2)
