@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: turn two rocprofv3 --pmc runs of this script "
                          "(FETCH_SIZE, WRITE_SIZE) into profiles/traffic_<workload>.json")
+    ap.add_argument("--page-budget", type=int, default=0, metavar="KP",
+                    help="select the KP best pages (of the workload's page size) per row "
+                         "instead of the top-k tokens, and attend to their positions")
     ap.add_argument("--commands", nargs="*", default=[],
                     help="with --traffic-summary: the commands that made the runs")
     return ap.parse_args()
@@ -68,22 +71,36 @@ def parse():
 # --------------------------------------------------------------------------
 
 
-def algorithmic_bytes(inp) -> dict:
+def algorithmic_bytes(inp, k_sel=None, page=0) -> dict:
+    """Compulsory bytes and MFMA flops of one step. With ``page`` > 0 the selection is a
+    page budget of k_sel / page pages: page maxima written and read (4 + 4 B per page),
+    pages and positions written, and every legal position of the kept pages attended."""
     wl = inp.wl
+    k_sel = wl.topk if k_sel is None else k_sel
     lens, qls = inp.seq_lens_host, inp.q_lens_host
     T = inp.total_q
     key_b = {"bf16": 2 * wl.idx_dim, "f32": 4 * wl.idx_dim, "fp8": wl.idx_dim + 4}[wl.idx_k_dtype]
     q_b = {"bf16": 2, "f32": 4}[wl.idx_q_dtype]
     valid = sum(sum(L - q + i + 1 for i in range(q)) for L, q in zip(lens, qls))  # (row, s) pairs
-    sel = sum(sum(min(wl.topk, L - q + i + 1) for i in range(q)) for L, q in zip(lens, qls))
+    if page:
+        kp = k_sel // page
+        # legal positions of the kp pages kept: all pages if the row has at most kp,
+        # else kp pages of which the last may be partial (bounded by kp full pages)
+        sel = sum(sum(min(kp * page, L - q + i + 1) for i in range(q)) for L, q in zip(lens, qls))
+        n_pages = sum(sum((L - q + i) // page + 1 for i in range(q)) for L, q in zip(lens, qls))
+    else:
+        sel = sum(sum(min(wl.topk, L - q + i + 1) for i in range(q)) for L, q in zip(lens, qls))
     pages = sum((L + wl.page_size - 1) // wl.page_size for L in lens)
     e = {"bf16": 2, "f32": 4}[wl.mla_dtype]
     row_b = (wl.d_latent + wl.d_rope) * e
     indexer = (sum(lens) * key_b + T * wl.idx_heads * (wl.idx_dim * q_b + 4) + 4 * valid
                + 4 * pages)
-    topk = 4 * valid + 4 * T * wl.topk
+    if page:
+        topk = 4 * valid + 8 * n_pages + 4 * T * (k_sel // page) + 4 * T * k_sel
+    else:
+        topk = 4 * valid + 4 * T * wl.topk
     mla_one = (sel * row_b + T * wl.mla_heads * (wl.d_latent + wl.d_rope) * e
-               + T * wl.topk * 4 + T * wl.mla_heads * (wl.d_latent + 1) * 4)
+               + T * k_sel * 4 + T * wl.mla_heads * (wl.d_latent + 1) * 4)
     flops_idx = 2 * wl.idx_heads * wl.idx_dim * valid
     flops_mla = 2 * wl.mla_heads * (2 * wl.d_latent + wl.d_rope) * sel
     return {"indexer": indexer, "topk": topk, "mla_per_layer": mla_one,
@@ -97,7 +114,7 @@ def algorithmic_bytes(inp) -> dict:
 # --------------------------------------------------------------------------
 
 
-def cpu_baseline(inp, budget_s: float):
+def cpu_baseline(inp, budget_s: float, kp: int = 0):
     from oracle import dsa_oracle as O
     from workloads import host_view
 
@@ -112,7 +129,8 @@ def cpu_baseline(inp, budget_s: float):
     done, t0 = 0, time.perf_counter()
     for r in order:
         s = O.indexer_scores(host, [int(r)])
-        idx = O.topk(s, inp.wl.topk)
+        idx = (O.page_budget_select(s, inp.wl.page_size, kp)[1] if kp
+               else O.topk(s, inp.wl.topk))
         for l in range(inp.wl.n_layers):
             O.sparse_mla(host, l, idx)
         done += 1
@@ -121,7 +139,9 @@ def cpu_baseline(inp, budget_s: float):
     dt = time.perf_counter() - t0
     return {"value": done / dt, "unit": "query tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {inp.total_q} query rows (random, seed 0), full pass per row "
-                      f"(indexer over all causal keys, top-{inp.wl.topk}, {inp.wl.n_layers} MLA "
+                      f"(indexer over all causal keys, "
+                      + (f"{kp}-page budget" if kp else f"top-{inp.wl.topk}")
+                      + f", {inp.wl.n_layers} MLA "
                       f"layer(s)), numpy float64, {dt:.1f} s"}
 
 
@@ -306,33 +326,55 @@ def main():
     keys = dsa.PagedCache(inp.k_cache, inp.k_scale)
     kvs = [dsa.PagedCache(c) for c in inp.kv_cache]
     scores = torch.empty((T, inp.max_seq_len), dtype=torch.float32, device=dev)
-    indices = torch.empty((T, wl.topk), dtype=torch.int32, device=dev)
+    page = wl.page_size
+    kp = args.page_budget
+    k_sel = kp * page if kp else wl.topk  # positions attention reads per row
+    indices = torch.empty((T, k_sel), dtype=torch.int32, device=dev)
+    if kp:
+        n_pages = -(-inp.max_seq_len // page)
+        page_sc = torch.empty((T, n_pages), dtype=torch.float32, device=dev)
+        pages_sel = torch.empty((T, kp), dtype=torch.int32, device=dev)
+        pk_bytes = dsa.page_topk_workspace_size(T, inp.max_seq_len, page, kp)
+        pk_ws = torch.empty(max(pk_bytes, 16), dtype=torch.uint8, device=dev) if pk_bytes else None
     outs = [torch.empty((T, wl.mla_heads, wl.d_latent), dtype=torch.float32, device=dev)
             for _ in range(wl.n_layers)]
     lses = [torch.empty((T, wl.mla_heads), dtype=torch.float32, device=dev)
             for _ in range(wl.n_layers)]
-    ws_bytes = dsa.sparse_mla_workspace_size(T, wl.mla_heads, wl.d_latent, wl.topk)
+    ws_bytes = dsa.sparse_mla_workspace_size(T, wl.mla_heads, wl.d_latent, k_sel)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     tk_bytes = dsa.topk_workspace_size(T, inp.max_seq_len, wl.topk)
     tk_ws = torch.empty(max(tk_bytes, 16), dtype=torch.uint8, device=dev) if tk_bytes else None
     flush = torch.ones(1 << 27, dtype=torch.int64, device=dev)  # 1 GiB, evicted by reading
     stream = torch.cuda.current_stream(dev)
-    n_ev = 3 + wl.n_layers
+    sel_names = ["page_scores", "page_topk"] if kp else ["topk"]
+    n_ev = 2 + len(sel_names) + wl.n_layers
 
     def step(evs=None):
+        e = 0
         if evs is not None:
-            evs[0].record(stream)
+            evs[e].record(stream)
         dsa.indexer_scores(batch, inp.q_idx, inp.w, keys, scores=scores)
+        e += 1
         if evs is not None:
-            evs[1].record(stream)
-        dsa.topk(batch, scores, wl.topk, indices=indices, workspace=tk_ws)
+            evs[e].record(stream)
+        if kp:
+            dsa.page_scores(batch, scores, page, out=page_sc)
+            e += 1
+            if evs is not None:
+                evs[e].record(stream)
+            dsa.page_topk(batch, page_sc, page, kp, pages=pages_sel, indices=indices,
+                          workspace=pk_ws)
+        else:
+            dsa.topk(batch, scores, wl.topk, indices=indices, workspace=tk_ws)
+        e += 1
         if evs is not None:
-            evs[2].record(stream)
+            evs[e].record(stream)
         for l in range(wl.n_layers):
             dsa.sparse_mla_fwd(batch, inp.q_mla[l], kvs[l], indices, wl.d_latent, wl.scale,
                                out=outs[l], lse=lses[l], workspace=ws)
+            e += 1
             if evs is not None:
-                evs[3 + l].record(stream)
+                evs[e].record(stream)
 
     def evict():
         if not args.no_flush:
@@ -394,13 +436,14 @@ def main():
     torch.cuda.synchronize()
     warm_ms = w0.elapsed_time(w1) / args.steps
 
-    ab = algorithmic_bytes(inp)
-    names = ["indexer", "topk"] + [f"mla_l{l}" for l in range(wl.n_layers)]
-    stage_bytes = [ab["indexer"], ab["topk"]] + [ab["mla_per_layer"]] * wl.n_layers
-    mla_ms = float(np.sum(stage_ms[2:]))
+    ab = algorithmic_bytes(inp, k_sel=k_sel, page=page if kp else 0)
+    names = ["indexer"] + sel_names + [f"mla_l{l}" for l in range(wl.n_layers)]
+    n_sel = len(sel_names)
+    mla_ms = float(np.sum(stage_ms[1 + n_sel:]))
+    sel_ms = float(np.sum(stage_ms[1:1 + n_sel]))
     kern = {"indexer": (float(stage_ms[0]), ab["indexer"], "dsa_indexer_scores",
                         ab["flops_indexer"]),
-            "topk": (float(stage_ms[1]), ab["topk"], "dsa_topk", 0),
+            "topk": (sel_ms, ab["topk"], "dsa_page_topk" if kp else "dsa_topk", 0),
             "sparse_mla": (mla_ms / wl.n_layers, ab["mla_per_layer"], "dsa_sparse_mla_fwd",
                            ab["flops_mla_per_layer"])}
     dom = max(kern, key=lambda k: kern[k][0] * (wl.n_layers if k == "sparse_mla" else 1))
@@ -432,6 +475,8 @@ def main():
         "config": {"workload": wl.name, "description": wl.description, "batch": wl.batch,
                    "total_q": T, "max_seq_len": inp.max_seq_len, "topk": wl.topk,
                    "page_size": wl.page_size, "mla_layers": wl.n_layers,
+                   "selection": (f"page budget: {kp} pages of {page} positions" if kp
+                                 else f"token top-{wl.topk}"),
                    "parallelism": "single GPU"},
         "achieved_hbm_gbs": ab["total"] / (ms * 1e-3) / 1e9,
         "algorithmic_bytes_per_step": ab["total"],
@@ -444,7 +489,7 @@ def main():
                    ("; HIP graph replay of the captured step" if args.graph
                     else "; plain stream launches")),
         "roofline": dict(roof, kernel=d_sym, kernels=STAGE_KERNELS[dom],
-                         traffic=committed_traffic(wl.name, dom),
+                         traffic=None if kp else committed_traffic(wl.name, dom),
                          algorithmic_bytes_per_launch=d_bytes, avg_launch_ms=d_ms),
         "wall_s_timed_loop": wall,
     }
@@ -457,7 +502,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if args.cpu_seconds > 0:
-        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, kp)
     print(json.dumps(line), flush=True)
 
 

@@ -210,6 +210,58 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_d
                               size_t workspace_bytes, void *stream);
 
 /*
+ * Page scores for page-budget selection, the alternative to token top-k that
+ * bounds the pages attention reads ("Making GLM-5.2 Sparse on TPUs", section
+ * "Make the sparsity unit match the memory unit": a page is ranked by its
+ * highest legal token score, and the causal and valid-length masks apply
+ * before that maximum, so an invisible token never promotes its page;
+ * section "Stream indexer scores over live context": the selection consumes
+ * page maxima).
+ *
+ * Pages are logical pages of page_size positions of the row's sequence (the
+ * block table plays no part). For row r and every page p <= t_r / page_size:
+ *   page_scores[r * ld_pages + p] = max { scores[r * ld_scores + s] :
+ *                                         p * page_size <= s < (p + 1) * page_size, s <= t_r }
+ * Pages past t_r / page_size are not written; scores past t_r are never read.
+ *
+ *   scores       device [total_q, ld_scores] fp32 token scores (dsa_indexer_scores)
+ *   page_scores  device [total_q, ld_pages] fp32 output, ld_pages >= ceil(max_seq_len / page_size)
+ *
+ * Errors: DSA_ERR_NULL, DSA_ERR_SHAPE (page_size < 1, short row strides, bad
+ * bounds, misaligned pointers), DSA_ERR_LAUNCH.
+ */
+dsa_status dsa_page_scores(const dsa_batch *batch, const float *scores, int64_t ld_scores,
+                           int32_t page_size, float *page_scores, int64_t ld_pages, void *stream);
+
+/* Bytes of workspace dsa_page_topk needs for these host bounds (0 if none). */
+size_t dsa_page_topk_workspace_size(int32_t total_q, int32_t max_seq_len, int32_t page_size,
+                                    int32_t kp);
+
+/*
+ * Page-budget selection (same sections): per row the kp pages with the
+ * highest page scores among pages 0 .. t_r / page_size, equal scores ordered
+ * by lower page first, listed in ascending page order and padded with -1:
+ * pages[r * kp + i]. With `indices` non-NULL, also the legal token positions
+ * of those pages, the index list of dsa_sparse_mla_fwd with k = kp * page_size:
+ *   indices[r * kp * page_size + i * page_size + o] = pages[r * kp + i] * page_size + o
+ * when that page is not -1 and the position is <= t_r, else -1 (ascending
+ * among the valid entries).
+ *
+ *   page_scores  device [total_q, ld_pages] fp32, as written by dsa_page_scores
+ *   pages        device [total_q, kp] int32 output (fully written)
+ *   indices      device [total_q, kp * page_size] int32 output (fully written), or NULL
+ *   workspace    device, >= dsa_page_topk_workspace_size(...) bytes (NULL when 0)
+ *
+ * Errors: DSA_ERR_NULL, DSA_ERR_SHAPE (page_size or kp < 1, short ld_pages,
+ * kp * page_size past int32, misaligned pointers), DSA_ERR_WORKSPACE,
+ * DSA_ERR_UNSUPPORTED (more pages per row than the selection handles),
+ * DSA_ERR_LAUNCH.
+ */
+dsa_status dsa_page_topk(const dsa_batch *batch, const float *page_scores, int64_t ld_pages,
+                         int32_t page_size, int32_t kp, int32_t *pages, int32_t *indices,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Append this step's new tokens to the paged caches, the write that precedes
  * selection ("GLM-5.2 on vLLM Ascend: Request-to-Backend Inference Path",
  * section "8. The SFA backend, step by step", "Write paged cache": the slot

@@ -375,3 +375,51 @@ def kv_append(slot_mapping, latent=None, kv_cache=None, idx_keys=None, key_cache
                 else:
                     key_out[s // P, s % P] = row
     return kv_out, key_out, scale_out
+
+
+# --------------------------------------------------------------------------
+# page-budget selection (an alternative to token top-k)
+# --------------------------------------------------------------------------
+
+
+def page_scores_row(token_scores: np.ndarray, page_size: int) -> np.ndarray:
+    """Score of each logical page of one row: the maximum of its legal token scores.
+
+    ("Making GLM-5.2 Sparse on TPUs", section "Make the sparsity unit match the
+    memory unit": a page is ranked by its highest legal token score, and the
+    causal and valid-length masks apply before the maximum.) ``token_scores``
+    holds exactly the legal positions 0..t of the row, so a page's maximum
+    never sees a position past t; the last page may be partial.
+    """
+    s = np.asarray(token_scores, dtype=np.float64)
+    n_pages = (len(s) + page_size - 1) // page_size
+    return np.array([s[p * page_size:(p + 1) * page_size].max() for p in range(n_pages)])
+
+
+def expand_pages(pages: np.ndarray, page_size: int, t: int) -> np.ndarray:
+    """Token positions read for the selected pages (same section: attention reads every
+    legal token of each kept page): slot i * page_size + o holds pages[i] * page_size + o
+    when the page is kept (not -1) and the position is <= t, else -1."""
+    out = np.full(len(pages) * page_size, -1, dtype=np.int32)
+    for i, p in enumerate(pages):
+        if p < 0:
+            continue
+        for o in range(page_size):
+            pos = int(p) * page_size + o
+            if pos <= t:
+                out[i * page_size + o] = pos
+    return out
+
+
+def page_budget_select(scores: Dict[int, np.ndarray], page_size: int, kp: int):
+    """Per row: (the kp best pages, ascending, -1 padded; their token positions).
+
+    Pages are ranked by page_scores_row and kept with the token top-k's rule
+    (higher score first, equal scores by lower page), then expanded.
+    """
+    pages, idx = {}, {}
+    for r, s in scores.items():
+        pr = topk_row(page_scores_row(s, page_size), kp)
+        pages[r] = pr
+        idx[r] = expand_pages(pr, page_size, len(s) - 1)
+    return pages, idx

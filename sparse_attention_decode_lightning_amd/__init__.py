@@ -30,6 +30,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "Batch", "PagedCache", "DSAError", "indexer_scores", "topk", "sparse_mla_fwd",
     "topk_workspace_size", "sparse_mla_workspace_size", "abi_version", "kv_append",
+    "page_scores", "page_topk", "page_topk_workspace_size",
 ]
 
 _DT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.uint8: DSA_FP8_E4M3,
@@ -144,6 +145,55 @@ def topk(batch: Batch, scores: torch.Tensor, k: int, indices: Optional[torch.Ten
                        _dev(indices, "indices", torch.int32), wp, wb, _stream(scores.device)),
           "dsa_topk")
     return indices
+
+
+def page_scores(batch: Batch, scores: torch.Tensor, page_size: int,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """[T, ld_pages] fp32: max of each logical page's legal token scores (pages past t_r
+    untouched)."""
+    T = scores.shape[0]
+    n_pages = max(1, -(-batch.max_seq_len // page_size))
+    if out is None:
+        out = torch.empty((T, n_pages), dtype=torch.float32, device=scores.device)
+    if out.dim() != 2 or out.shape[0] != T:
+        raise ValueError("page scores must be [T, ld_pages]")
+    b = batch.c()
+    check(lib.dsa_page_scores(ctypes.byref(b), _dev(scores, "scores", torch.float32),
+                              scores.shape[1], page_size, _dev(out, "page_scores", torch.float32),
+                              out.shape[1], _stream(scores.device)), "dsa_page_scores")
+    return out
+
+
+def page_topk_workspace_size(total_q: int, max_seq_len: int, page_size: int, kp: int) -> int:
+    return int(lib.dsa_page_topk_workspace_size(total_q, max_seq_len, page_size, kp))
+
+
+def page_topk(batch: Batch, page_scores: torch.Tensor, page_size: int, kp: int,
+              pages: Optional[torch.Tensor] = None, indices: Optional[torch.Tensor] = None,
+              want_indices: bool = True, workspace: Optional[torch.Tensor] = None):
+    """(pages [T, kp], indices [T, kp * page_size] or None): the kp best pages per row
+    (ascending, -1 padded) and their legal token positions."""
+    T = page_scores.shape[0]
+    dev = page_scores.device
+    if pages is None:
+        pages = torch.empty((T, kp), dtype=torch.int32, device=dev)
+    if indices is None and want_indices:
+        indices = torch.empty((T, kp * page_size), dtype=torch.int32, device=dev)
+    if tuple(pages.shape) != (T, kp):
+        raise ValueError("pages must be [T, kp]")
+    if indices is not None and tuple(indices.shape) != (T, kp * page_size):
+        raise ValueError("indices must be [T, kp * page_size]")
+    need = page_topk_workspace_size(batch.total_q, batch.max_seq_len, page_size, kp)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wp = 0 if workspace is None else _dev(workspace, "workspace")
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    b = batch.c()
+    check(lib.dsa_page_topk(ctypes.byref(b), _dev(page_scores, "page_scores", torch.float32),
+                            page_scores.shape[1], page_size, kp, _dev(pages, "pages", torch.int32),
+                            0 if indices is None else _dev(indices, "indices", torch.int32),
+                            wp, wb, _stream(dev)), "dsa_page_topk")
+    return pages, indices
 
 
 def sparse_mla_workspace_size(total_q: int, n_heads: int, d_latent: int, k: int) -> int:

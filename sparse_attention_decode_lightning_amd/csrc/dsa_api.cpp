@@ -126,7 +126,7 @@ dsa_status dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld_scor
   const size_t need = dsa::topk_workspace_bytes(bt.total_q, bt.max_seq_len, k);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
     return DSA_ERR_WORKSPACE;
-  return launch_status(dsa::launch_topk(bt, scores, ld_scores, k, indices, workspace,
+  return launch_status(dsa::launch_topk(bt, scores, ld_scores, k, 1, indices, workspace,
                                         workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
@@ -165,6 +165,48 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_d
   return launch_status(dsa::launch_sparse_mla(bt, q, q_dtype, n_heads, d_latent, d_rope, kc,
                                               indices, k, scale, out, lse, workspace,
                                               workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+dsa_status dsa_page_scores(const dsa_batch *batch, const float *scores, int64_t ld_scores,
+                           int32_t page_size, float *page_scores, int64_t ld_pages, void *stream) {
+  BatchArgs bt;
+  const dsa_status st = check_batch(batch, &bt);
+  if (st != DSA_OK) return st;
+  if (scores == nullptr || page_scores == nullptr) return DSA_ERR_NULL;
+  if (page_size < 1 || ld_scores < bt.max_seq_len || ld_scores < 1) return DSA_ERR_SHAPE;
+  if (ld_pages < dsa::candidate_bound(bt.max_seq_len, page_size) || ld_pages < 1)
+    return DSA_ERR_SHAPE;
+  if (!aligned(scores, 4) || !aligned(page_scores, 4)) return DSA_ERR_SHAPE;
+  return launch_status(dsa::launch_page_scores(bt, scores, ld_scores, page_size, page_scores,
+                                               ld_pages, static_cast<hipStream_t>(stream)));
+}
+
+size_t dsa_page_topk_workspace_size(int32_t total_q, int32_t max_seq_len, int32_t page_size,
+                                    int32_t kp) {
+  if (page_size < 1) return 0;
+  return dsa::topk_workspace_bytes(total_q, dsa::candidate_bound(max_seq_len, page_size), kp);
+}
+
+dsa_status dsa_page_topk(const dsa_batch *batch, const float *page_scores, int64_t ld_pages,
+                         int32_t page_size, int32_t kp, int32_t *pages, int32_t *indices,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  BatchArgs bt;
+  const dsa_status st = check_batch(batch, &bt);
+  if (st != DSA_OK) return st;
+  if (page_scores == nullptr || pages == nullptr) return DSA_ERR_NULL;
+  if (page_size < 1 || kp < 1) return DSA_ERR_SHAPE;
+  const int32_t max_pages = dsa::candidate_bound(bt.max_seq_len, page_size);
+  if (ld_pages < max_pages || ld_pages < 1) return DSA_ERR_SHAPE;
+  if ((int64_t)kp * page_size > (int64_t)0x7FFFFFFF) return DSA_ERR_SHAPE;
+  if (!aligned(page_scores, 4) || !aligned(pages, 4) || (indices != nullptr && !aligned(indices, 4)))
+    return DSA_ERR_SHAPE;
+  if (!dsa::topk_supported(max_pages, kp)) return DSA_ERR_UNSUPPORTED;
+  const size_t need = dsa::topk_workspace_bytes(bt.total_q, max_pages, kp);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+    return DSA_ERR_WORKSPACE;
+  return launch_status(dsa::launch_page_topk(bt, page_scores, ld_pages, page_size, kp, pages,
+                                             indices, workspace, workspace_bytes,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 dsa_status dsa_kv_append(const int32_t *slot_mapping, int32_t n_tokens, const void *latent,

@@ -35,10 +35,14 @@ hipError_t launch_indexer_scores(const BatchArgs &bt, const void *q_idx, int32_t
                                  const CacheArgs &keys, float *scores, int64_t ld_scores,
                                  hipStream_t stream);
 
-size_t topk_workspace_bytes(int32_t total_q, int32_t max_seq_len, int32_t k);
-bool topk_supported(int32_t max_seq_len, int32_t k);
+// Top-k over candidates: positions (unit 1) or pages of `unit` positions;
+// sizes and support are in candidates per row (candidate_bound of the batch).
+int candidate_bound(int32_t max_seq_len, int32_t unit);
+size_t topk_workspace_bytes(int32_t total_q, int32_t max_cands, int32_t k);
+bool topk_supported(int32_t max_cands, int32_t k);
 hipError_t launch_topk(const BatchArgs &bt, const float *scores, int64_t ld_scores, int32_t k,
-                       int32_t *indices, void *workspace, size_t ws_bytes, hipStream_t stream);
+                       int32_t unit, int32_t *indices, void *workspace, size_t ws_bytes,
+                       hipStream_t stream);
 
 int mla_num_splits(int32_t total_q, int32_t n_heads, int32_t d_latent, int32_t k);
 int mla_max_k();  // largest k of the 64-head bf16 MFMA path
@@ -47,6 +51,13 @@ hipError_t launch_sparse_mla(const BatchArgs &bt, const void *q, int32_t q_dtype
                              int32_t d_latent, int32_t d_rope, const CacheArgs &kv,
                              const int32_t *indices, int32_t k, float scale, float *out, float *lse,
                              void *workspace, size_t ws_bytes, hipStream_t stream);
+
+hipError_t launch_page_scores(const BatchArgs &bt, const float *scores, int64_t ld,
+                              int32_t page_size, float *page_scores, int64_t ld_pages,
+                              hipStream_t stream);
+hipError_t launch_page_topk(const BatchArgs &bt, const float *page_scores, int64_t ld_pages,
+                            int32_t page_size, int32_t kp, int32_t *pages, int32_t *indices,
+                            void *workspace, size_t ws_bytes, hipStream_t stream);
 
 hipError_t launch_kv_append(const int32_t *slots, int32_t n_tokens, const void *latent,
                             const CacheArgs *kv, const void *keys, int32_t key_dtype,

@@ -30,6 +30,15 @@
 namespace dsa {
 namespace {
 
+// Candidates of a row: its positions 0..t (unit 1), or the groups of `unit`
+// consecutive positions (pages) that hold them, 0..t / unit; none when the
+// row has no position.
+__device__ __forceinline__ int row_cands(const int32_t *cu_q, const int32_t *seq_lens, int batch,
+                                         int total_q, int max_seq_len, int row, FastDiv unit) {
+  const int t = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row).t;
+  return t < 0 ? 0 : (int)fast_div((uint32_t)t, unit) + 1;
+}
+
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kChunk = 32768;  // candidates per workgroup (keys cached in LDS)
@@ -203,7 +212,8 @@ __device__ void ordered_emit(const uint32_t *keys, int n, uint32_t tau, uint32_t
 template <bool PHASE1>
 __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
-    int total_q, int max_seq_len, const float *__restrict__ scores, int64_t ld, int k,
+    int total_q, int max_seq_len, int n_max, FastDiv unit, const float *__restrict__ scores,
+    int64_t ld, int k,
     int32_t *__restrict__ indices, int n_chunks, uint32_t *__restrict__ ws_key,
     int32_t *__restrict__ ws_pos) {
   extern __shared__ uint32_t s_keys[];
@@ -211,7 +221,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
   const int row = PHASE1 ? blockIdx.x / n_chunks : blockIdx.x;
   const int chunk = PHASE1 ? blockIdx.x % n_chunks : 0;
   const int tid = threadIdx.x;
-  const int n_row = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row).t + 1;
+  const int n_row = row_cands(cu_q, seq_lens, batch, total_q, max_seq_len, row, unit);
   if (!PHASE1 && n_row <= k) {
     int32_t *out = indices + (int64_t)row * k;
     for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n_row ? i : -1;
@@ -248,14 +258,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
 // Phase 2: top-k among the concatenated chunk survivors of one row.
 __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
-    int total_q, int max_seq_len, int k, int n_chunks, const uint32_t *__restrict__ ws_key,
+    int total_q, int max_seq_len, int n_max, FastDiv unit, int k, int n_chunks,
+    const uint32_t *__restrict__ ws_key,
     const int32_t *__restrict__ ws_pos, int32_t *__restrict__ indices) {
   extern __shared__ uint32_t s_keys[];
   __shared__ TopkShared sh;
   __shared__ int s_start[64];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
-  const int n_row = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row).t + 1;
+  const int n_row = row_cands(cu_q, seq_lens, batch, total_q, max_seq_len, row, unit);
   int32_t *out = indices + (int64_t)row * k;
   if (n_row <= k) {
     for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n_row ? i : -1;
@@ -321,7 +332,8 @@ constexpr int kRegThreads = 1024;
 template <int NT, int R>
 __global__ __launch_bounds__(NT) void topk_reg_kernel(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
-    int total_q, int max_seq_len, const float *__restrict__ scores, int64_t ld, int k,
+    int total_q, int max_seq_len, int n_max, FastDiv unit, const float *__restrict__ scores,
+    int64_t ld, int k,
     int32_t *__restrict__ indices) {
   constexpr int kRegThreads = NT;
   __shared__ SelectShared<NT / kWave, R> sh;
@@ -332,10 +344,10 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(
 #pragma unroll
   for (int u = 0; u < R; ++u) {
     const int i = u * kRegThreads + tid;
-    v[u] = i < max_seq_len ? src[i] : 0.0f;
+    v[u] = i < n_max ? src[i] : 0.0f;
   }
   select_clear(sh);
-  const int n = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row).t + 1;
+  const int n = row_cands(cu_q, seq_lens, batch, total_q, max_seq_len, row, unit);
   int32_t *out = indices + (int64_t)row * k;
   if (n <= k) {
     for (int i = tid; i < k; i += kRegThreads) out[i] = i < n ? i : -1;
@@ -368,7 +380,8 @@ bool split_path(int32_t max_seq_len, int32_t k) {
 
 __global__ __launch_bounds__(kRegThreads) void topk_chunk_kernel(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
-    int total_q, int max_seq_len, const float *__restrict__ scores, int64_t ld, int k, int nc,
+    int total_q, int max_seq_len, int n_max, FastDiv unit, const float *__restrict__ scores,
+    int64_t ld, int k, int nc,
     uint32_t *__restrict__ ws_key, int32_t *__restrict__ ws_pos) {
   constexpr int R = kSplitChunk / kRegThreads;
   __shared__ SelectShared<kRegThreads / kWave, R> sh;
@@ -380,10 +393,10 @@ __global__ __launch_bounds__(kRegThreads) void topk_chunk_kernel(
 #pragma unroll
   for (int u = 0; u < R; ++u) {
     const int i = u * kRegThreads + tid;
-    v[u] = base + i < max_seq_len ? src[i] : 0.0f;
+    v[u] = base + i < n_max ? src[i] : 0.0f;
   }
   select_clear(sh);
-  const int n = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row).t + 1;
+  const int n = row_cands(cu_q, seq_lens, batch, total_q, max_seq_len, row, unit);
   const int m = min(max(n - base, 0), kSplitChunk);  // candidates of this chunk
   uint32_t *okey = ws_key + ((int64_t)row * nc + c) * k;
   int32_t *opos = ws_pos + ((int64_t)row * nc + c) * k;
@@ -410,13 +423,14 @@ __global__ __launch_bounds__(kRegThreads) void topk_chunk_kernel(
 template <int R>
 __global__ __launch_bounds__(kRegThreads) void topk_split_merge_kernel(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
-    int total_q, int max_seq_len, int k, FastDiv kdiv, int nc, const uint32_t *__restrict__ ws_key,
+    int total_q, int max_seq_len, int n_max, FastDiv unit, int k, FastDiv kdiv, int nc,
+    const uint32_t *__restrict__ ws_key,
     const int32_t *__restrict__ ws_pos, int32_t *__restrict__ indices) {
   __shared__ SelectShared<kRegThreads / kWave, R> sh;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   select_clear(sh);
-  const int n = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row).t + 1;
+  const int n = row_cands(cu_q, seq_lens, batch, total_q, max_seq_len, row, unit);
   int32_t *out = indices + (int64_t)row * k;
   if (n <= k) {
     for (int i = tid; i < k; i += kRegThreads) out[i] = i < n ? i : -1;
@@ -449,6 +463,10 @@ hipError_t set_lds(const void *fn, size_t bytes) {
 
 }  // namespace
 
+int candidate_bound(int32_t max_seq_len, int32_t unit) {
+  return unit <= 1 ? max_seq_len : (int)(((int64_t)max_seq_len + unit - 1) / unit);
+}
+
 size_t topk_workspace_bytes(int32_t total_q, int32_t max_seq_len, int32_t k) {
   if (total_q < 1 || k < 1) return 0;
   const size_t per = (size_t)total_q * k * (sizeof(uint32_t) + sizeof(int32_t));
@@ -464,55 +482,60 @@ bool topk_supported(int32_t max_seq_len, int32_t k) {
 }
 
 hipError_t launch_topk(const BatchArgs &bt, const float *scores, int64_t ld, int32_t k,
-                       int32_t *indices, void *workspace, size_t, hipStream_t stream) {
+                       int32_t unit, int32_t *indices, void *workspace, size_t,
+                       hipStream_t stream) {
   if (bt.total_q == 0) return hipSuccess;
-  if (bt.max_seq_len <= 32 * kRegThreads) {
-    auto kernel = bt.max_seq_len <= 8 * kRegThreads    ? topk_reg_kernel<kRegThreads, 8>
-                  : bt.max_seq_len <= 16 * kRegThreads ? topk_reg_kernel<kRegThreads, 16>
-                                                       : topk_reg_kernel<kRegThreads, 32>;
+  // candidates of a row: positions (unit 1) or groups of `unit` positions
+  const int n_max = candidate_bound(bt.max_seq_len, unit);
+  const FastDiv fu = make_fast_div((uint32_t)unit);
+  if (n_max <= 32 * kRegThreads) {
+    auto kernel = n_max <= 8 * kRegThreads    ? topk_reg_kernel<kRegThreads, 8>
+                  : n_max <= 16 * kRegThreads ? topk_reg_kernel<kRegThreads, 16>
+                                              : topk_reg_kernel<kRegThreads, 32>;
     hipLaunchKernelGGL(kernel, dim3(bt.total_q), dim3(kRegThreads), 0, stream, bt.seq_lens,
-                       bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, scores, ld, k, indices);
+                       bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, n_max, fu, scores, ld, k,
+                       indices);
     return hipGetLastError();
   }
   hipError_t e;
-  if (split_path(bt.max_seq_len, k)) {
-    const int nc = split_chunks(bt.max_seq_len);
+  if (split_path(n_max, k)) {
+    const int nc = split_chunks(n_max);
     if (bt.total_q > 65535) return hipErrorInvalidConfiguration;
     uint32_t *ws_key = static_cast<uint32_t *>(workspace);
     int32_t *ws_pos = reinterpret_cast<int32_t *>(ws_key + (size_t)bt.total_q * nc * k);
     hipLaunchKernelGGL(topk_chunk_kernel, dim3(nc, bt.total_q), dim3(kRegThreads), 0, stream,
-                       bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, scores, ld, k,
-                       nc, ws_key, ws_pos);
+                       bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, n_max, fu,
+                       scores, ld, k, nc, ws_key, ws_pos);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t cands = (int64_t)nc * k;
     auto merge = cands <= 8 * kRegThreads    ? topk_split_merge_kernel<8>
                  : cands <= 16 * kRegThreads ? topk_split_merge_kernel<16>
                                              : topk_split_merge_kernel<32>;
     hipLaunchKernelGGL(merge, dim3(bt.total_q), dim3(kRegThreads), 0, stream, bt.seq_lens,
-                       bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, k,
+                       bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, n_max, fu, k,
                        make_fast_div((uint32_t)k), nc, ws_key, ws_pos, indices);
     return hipGetLastError();
   }
   const size_t lds = (size_t)kChunk * sizeof(uint32_t);
-  if (!two_phase(bt.max_seq_len)) {
+  if (!two_phase(n_max)) {
     if ((e = set_lds((const void *)topk_rows_kernel<false>, lds)) != hipSuccess) return e;
     hipLaunchKernelGGL(topk_rows_kernel<false>, dim3(bt.total_q), dim3(kTopkThreads), lds, stream,
-                       bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, scores, ld, k,
-                       indices, 1, nullptr, nullptr);
+                       bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, n_max, fu,
+                       scores, ld, k, indices, 1, nullptr, nullptr);
     return hipGetLastError();
   }
-  const int nc = chunks_of(bt.max_seq_len);
+  const int nc = chunks_of(n_max);
   uint32_t *ws_key = static_cast<uint32_t *>(workspace);
   int32_t *ws_pos = reinterpret_cast<int32_t *>(ws_key + (size_t)bt.total_q * nc * k);
   if ((e = set_lds((const void *)topk_rows_kernel<true>, lds)) != hipSuccess) return e;
   if ((e = set_lds((const void *)topk_merge_kernel, lds)) != hipSuccess) return e;
   hipLaunchKernelGGL(topk_rows_kernel<true>, dim3(bt.total_q * nc), dim3(kTopkThreads), lds,
-                     stream, bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, scores,
-                     ld, k, indices, nc, ws_key, ws_pos);
+                     stream, bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, n_max,
+                     fu, scores, ld, k, indices, nc, ws_key, ws_pos);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(topk_merge_kernel, dim3(bt.total_q), dim3(kTopkThreads), lds, stream,
-                     bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, k, nc, ws_key,
-                     ws_pos, indices);
+                     bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, n_max, fu, k, nc,
+                     ws_key, ws_pos, indices);
   return hipGetLastError();
 }
 

@@ -6,6 +6,8 @@ are sensitive to the mistakes they are meant to catch, rather than merely
 passing.
 """
 
+import os
+
 import numpy as np
 import pytest
 
@@ -114,7 +116,26 @@ def _scale_by_255(k):
     return O.e4m3fn_encode(np.clip(k / sigma, -448, 448).astype(np.float32)), sigma
 
 
+def _page_sum(token_scores, page_size):
+    # rank a page by the sum of its scores instead of the maximum
+    s = np.asarray(token_scores, dtype=np.float64)
+    n = (len(s) + page_size - 1) // page_size
+    return np.array([s[p * page_size:(p + 1) * page_size].sum() for p in range(n)])
+
+
+def _expand_past_t(pages, page_size, t):
+    # read whole pages, also the positions past t
+    out = np.full(len(pages) * page_size, -1, dtype=np.int32)
+    for i, p in enumerate(pages):
+        if p >= 0:
+            out[i * page_size:(i + 1) * page_size] = np.arange(p * page_size, (p + 1) * page_size)
+    return out
+
+
 MUTATIONS = [
+    ("page_scores_row", _page_sum, ["test_page_budget_worked_example",
+                                    "test_page_budget_brute_force_with_masked_future"]),
+    ("expand_pages", _expand_past_t, ["test_page_budget_brute_force_with_masked_future"]),
     ("e4m3fn_encode", _e4m3_ties_away, ["test_e4m3_encode_round_trip_and_ties_to_even",
                                         "test_e4m3_encode_matches_torch_cast"]),
     ("e4m3fn_encode", _e4m3_truncate, ["test_e4m3_encode_round_trip_and_ties_to_even",
@@ -144,6 +165,8 @@ def _call(name):
     fn = getattr(pins, name)
     if name == "test_topk_brute_force_and_invariants":
         return fn(64, 16)
+    if name == "test_page_budget_worked_example":
+        return fn(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden"))
     return fn()
 
 

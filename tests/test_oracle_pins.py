@@ -519,3 +519,79 @@ def test_kv_append_writes_only_mapped_slots():
     kv3, keys3, _ = O.kv_append(slots, lat, kv, new_k.astype(np.float32), keys, None,
                                 key_cache_dtype="f32")
     assert keys3.dtype == keys.dtype and np.array_equal(kv3, kv2)
+
+
+# --------------------------------------------------------------------------
+# page-budget selection
+# --------------------------------------------------------------------------
+
+
+def _golden_page_example(golden):
+    d = {}
+    for ln in open(os.path.join(golden, "page_budget_example.txt")):
+        if ln.startswith("#") or not ln.strip():
+            continue
+        key, *vals = ln.split()
+        d[key] = [float(v) for v in vals]
+    return d
+
+
+def test_page_budget_worked_example(golden_dir):
+    """The pages' printed example: token top-4 names four positions, expanding their pages
+    reads sixteen, a two-page budget reads eight (tests/golden/page_budget_example.txt)."""
+    d = _golden_page_example(golden_dir)
+    P, k, kp = int(d["page_size"][0]), int(d["token_topk"][0]), int(d["page_budget"][0])
+    s = np.array(d["scores"])
+    tok = O.topk_row(s, k)
+    assert list(tok) == [int(v) for v in d["token_positions"]]
+    assert len({int(p) // P for p in tok}) * P == int(d["expanded_pages_reads"][0])
+    pages, idx = O.page_budget_select({0: s}, P, kp)
+    assert list(pages[0]) == [int(v) for v in d["budget_pages"]]
+    assert int((idx[0] >= 0).sum()) == int(d["budget_reads"][0])
+    assert list(idx[0]) == [p * P + o for p in pages[0] for o in range(P)]
+
+
+def test_page_budget_brute_force_with_masked_future():
+    """Brute force on tiny rows: a page's score is the maximum of its positions <= t only
+    (a huge score past t must not promote its page); kp best pages by (score desc, page asc)."""
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        P = int(rng.choice([1, 2, 4, 8]))
+        L = int(rng.integers(1, 40))
+        t = int(rng.integers(0, L))
+        kp = int(rng.integers(1, 6))
+        full = rng.choice([0.0, 1.0, 2.0, 3.0], L) + rng.random(L) * (trial % 2)
+        full[t + 1:] = 1e30  # positions past t: invisible
+        legal = full[: t + 1]
+        pages, idx = O.page_budget_select({0: legal}, P, kp)
+        n_pages = t // P + 1
+        best = []
+        for p in range(n_pages):
+            m = max(full[s] for s in range(p * P, min((p + 1) * P, L)) if s <= t)
+            best.append((-m, p))
+        want = sorted(p for _, p in sorted(best)[:kp])
+        got = [int(p) for p in pages[0] if p >= 0]
+        assert got == want, (trial, P, t, kp)
+        assert list(pages[0][len(want):]) == [-1] * (kp - len(want))
+        toks = [int(v) for v in idx[0] if v >= 0]
+        assert toks == [p * P + o for p in want for o in range(P) if p * P + o <= t]
+
+
+def test_page_budget_unit_pages_is_token_topk():
+    """Special case: pages of one position make page-budget selection token top-k."""
+    rng = np.random.default_rng(12)
+    for _ in range(10):
+        s = rng.standard_normal(int(rng.integers(5, 60)))
+        s[rng.integers(0, len(s), 3)] = s[0]  # some ties
+        k = int(rng.integers(1, 10))
+        pages, idx = O.page_budget_select({0: s}, 1, k)
+        assert np.array_equal(pages[0], O.topk_row(s, k))
+        assert np.array_equal(idx[0], O.topk_row(s, k))
+
+
+def test_page_budget_large_budget_reads_every_legal_position():
+    """A budget covering every page reads every position 0..t exactly once."""
+    s = np.random.default_rng(13).standard_normal(37)
+    pages, idx = O.page_budget_select({0: s}, 8, 5)
+    assert list(pages[0]) == [0, 1, 2, 3, 4]
+    assert [int(v) for v in idx[0] if v >= 0] == list(range(37))

@@ -1,0 +1,105 @@
+"""GPU parity of page-budget selection (dsa_page_scores, dsa_page_topk) against the oracle.
+
+Page maxima are compared bit-exact on the GPU's own token scores, with the
+score buffer past each row's causal bound filled with huge values (a page's
+maximum must never see them); the page top-k and its token expansion are
+compared bit-exact on the GPU's own page scores; attention over the expanded
+positions within the 1e-2 RMS bar. Pages of one position must reproduce the
+token top-k exactly, on a row long enough for the two-phase selection.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa_oracle as O
+from tests import parity as P
+from workloads import host_view, make_inputs, small_variant, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _dsa():
+    import sparse_attention_decode_lightning_amd as dsa
+    return dsa
+
+
+def _scores_with_poison(inp, dsa, b):
+    T, ld = inp.total_q, max(1, inp.max_seq_len)
+    scores = torch.full((T, ld), 3.0e38, dtype=torch.float32, device=inp.q_idx.device)
+    dsa.indexer_scores(b, inp.q_idx, inp.w, P.keys_of(inp), scores=scores)
+    return scores
+
+
+CASES = [
+    # (base workload, overrides, page size, page budget)
+    ("decode_b32_l8k", dict(batch=3, lens=(1500, 700, 64), topk=256), 64, 8),
+    ("verify_b8_l240k", dict(batch=2, lens=(3000, 1100), topk=256), 64, 5),
+    ("decode_b32_l8k", dict(batch=2, lens=(2000, 513), topk=256, page_size=16), 16, 20),
+    ("tiny", dict(), 16, 3),
+]
+
+
+@pytest.mark.parametrize("base,kw,page,kp", CASES, ids=[f"{c[0]}-P{c[2]}-kp{c[3]}" for c in CASES])
+def test_page_budget_matches_oracle(base, kw, page, kp):
+    dsa = _dsa()
+    wl = small_variant(base, **kw)
+    inp_h = make_inputs(wl)
+    inp = to_device(inp_h, torch.device("cuda:0"))
+    host = host_view(inp_h)
+    b = P.batch_of(inp)
+    scores = _scores_with_poison(inp, dsa, b)
+    n_pages = -(-inp.max_seq_len // page)
+    ps = torch.full((inp.total_q + 1, n_pages), float("nan"), dtype=torch.float32,
+                    device=scores.device)
+    dsa.page_scores(b, scores, page, out=ps[: inp.total_q])
+    pages, idx = dsa.page_topk(b, ps[: inp.total_q], page, kp)
+    torch.cuda.synchronize()
+    assert torch.isnan(ps[inp.total_q]).all(), "write past the page scores"
+    _, pos = P.positions(inp)
+    s = scores.double().cpu().numpy()
+    g_ps = ps[: inp.total_q].double().cpu().numpy()
+    g_pages = pages.cpu().numpy()
+    g_idx = idx.cpu().numpy()
+    for r in range(inp.total_q):
+        t = int(pos[r])
+        ref_ps = O.page_scores_row(s[r, : t + 1], page)
+        n = len(ref_ps)
+        assert np.array_equal(g_ps[r, :n], ref_ps), f"row {r}: page maxima differ"
+        assert np.isnan(g_ps[r, n:]).all(), f"row {r}: wrote a page past t"
+        ref_pages = O.topk_row(g_ps[r, :n], kp)
+        assert np.array_equal(g_pages[r], ref_pages), f"row {r}: page top-k differs"
+        assert np.array_equal(g_idx[r], O.expand_pages(ref_pages, page, t)), f"row {r}: expansion"
+    # attention over the expanded positions
+    out, lse = dsa.sparse_mla_fwd(b, inp.q_mla[0], dsa.PagedCache(inp.kv_cache[0]), idx,
+                                  wl.d_latent, wl.scale)
+    torch.cuda.synchronize()
+    P.check_mla(inp, 0, idx, out, lse, list(range(inp.total_q)), host)
+
+
+def test_unit_pages_reproduce_token_topk_on_long_rows():
+    """Pages of one position: dsa_page_topk == dsa_topk, on rows long enough (40,000
+    positions) for the two-phase selection."""
+    dsa = _dsa()
+    wl = small_variant("verify_b8_l240k", batch=2, lens=(40000, 35001), q_per_seq=2, topk=2048,
+                       page_size=64)
+    inp = to_device(make_inputs(wl), torch.device("cuda:0"))
+    b = P.batch_of(inp)
+    scores = _scores_with_poison(inp, dsa, b)
+    ps = dsa.page_scores(b, scores, 1)
+    pages, idx = dsa.page_topk(b, ps, 1, wl.topk)
+    tok = dsa.topk(b, scores, wl.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(pages, tok) and torch.equal(idx, tok)
+
+
+def test_page_topk_rejects_bad_arguments():
+    dsa = _dsa()
+    wl = small_variant("tiny")
+    inp = to_device(make_inputs(wl), torch.device("cuda:0"))
+    b = P.batch_of(inp)
+    ps = torch.zeros((inp.total_q, 16), dtype=torch.float32, device=inp.q_idx.device)
+    with pytest.raises(dsa.DSAError):
+        dsa.page_topk(b, ps, 16, 0)
+    with pytest.raises(dsa.DSAError):  # ld_pages shorter than ceil(max_seq_len / page)
+        dsa.page_topk(b, ps[:, :3], 16, 2)
