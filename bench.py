@@ -71,7 +71,7 @@ def parse():
 # --------------------------------------------------------------------------
 
 
-def algorithmic_bytes(inp, k_sel=None, page=0) -> dict:
+def algorithmic_bytes(inp, k_sel=None, page=0, fused=False) -> dict:
     """Compulsory bytes and MFMA flops of one step. With ``page`` > 0 the selection is a
     page budget of k_sel / page pages: page maxima written and read (4 + 4 B per page),
     pages and positions written, and every legal position of the kept pages attended."""
@@ -95,7 +95,10 @@ def algorithmic_bytes(inp, k_sel=None, page=0) -> dict:
     row_b = (wl.d_latent + wl.d_rope) * e
     indexer = (sum(lens) * key_b + T * wl.idx_heads * (wl.idx_dim * q_b + 4) + 4 * valid
                + 4 * pages)
-    if page:
+    if page and fused:  # page maxima come out of the indexer: no token score in memory
+        indexer = indexer - 4 * valid + 4 * n_pages
+        topk = 4 * n_pages + 4 * T * (k_sel // page) + 4 * T * k_sel
+    elif page:
         topk = 4 * valid + 8 * n_pages + 4 * T * (k_sel // page) + 4 * T * k_sel
     else:
         topk = 4 * valid + 4 * T * wl.topk
@@ -346,22 +349,35 @@ def main():
     tk_ws = torch.empty(max(tk_bytes, 16), dtype=torch.uint8, device=dev) if tk_bytes else None
     flush = torch.ones(1 << 27, dtype=torch.int64, device=dev)  # 1 GiB, evicted by reading
     stream = torch.cuda.current_stream(dev)
-    sel_names = ["page_scores", "page_topk"] if kp else ["topk"]
+    # page budget: page maxima straight from the indexer where it streams the keys,
+    # else token scores then their page maxima
+    fused = False
+    if kp:
+        try:
+            dsa.indexer_page_scores(batch, inp.q_idx, inp.w, keys, page, out=page_sc)
+            fused = True
+        except dsa.DSAError:
+            fused = False
+    sel_names = (["page_topk"] if fused else ["page_scores", "page_topk"]) if kp else ["topk"]
     n_ev = 2 + len(sel_names) + wl.n_layers
 
     def step(evs=None):
         e = 0
         if evs is not None:
             evs[e].record(stream)
-        dsa.indexer_scores(batch, inp.q_idx, inp.w, keys, scores=scores)
+        if fused:
+            dsa.indexer_page_scores(batch, inp.q_idx, inp.w, keys, page, out=page_sc)
+        else:
+            dsa.indexer_scores(batch, inp.q_idx, inp.w, keys, scores=scores)
         e += 1
         if evs is not None:
             evs[e].record(stream)
-        if kp:
+        if kp and not fused:
             dsa.page_scores(batch, scores, page, out=page_sc)
             e += 1
             if evs is not None:
                 evs[e].record(stream)
+        if kp:
             dsa.page_topk(batch, page_sc, page, kp, pages=pages_sel, indices=indices,
                           workspace=pk_ws)
         else:
@@ -436,7 +452,7 @@ def main():
     torch.cuda.synchronize()
     warm_ms = w0.elapsed_time(w1) / args.steps
 
-    ab = algorithmic_bytes(inp, k_sel=k_sel, page=page if kp else 0)
+    ab = algorithmic_bytes(inp, k_sel=k_sel, page=page if kp else 0, fused=fused)
     names = ["indexer"] + sel_names + [f"mla_l{l}" for l in range(wl.n_layers)]
     n_sel = len(sel_names)
     mla_ms = float(np.sum(stage_ms[1 + n_sel:]))
@@ -475,7 +491,8 @@ def main():
         "config": {"workload": wl.name, "description": wl.description, "batch": wl.batch,
                    "total_q": T, "max_seq_len": inp.max_seq_len, "topk": wl.topk,
                    "page_size": wl.page_size, "mla_layers": wl.n_layers,
-                   "selection": (f"page budget: {kp} pages of {page} positions" if kp
+                   "selection": (f"page budget: {kp} pages of {page} positions"
+                                 + (", page maxima from the indexer" if fused else "") if kp
                                  else f"token top-{wl.topk}"),
                    "parallelism": "single GPU"},
         "achieved_hbm_gbs": ab["total"] / (ms * 1e-3) / 1e9,

@@ -233,6 +233,28 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_d
 dsa_status dsa_page_scores(const dsa_batch *batch, const float *scores, int64_t ld_scores,
                            int32_t page_size, float *page_scores, int64_t ld_pages, void *stream);
 
+/*
+ * The same page scores straight from the indexer, with no token score in
+ * memory ("Making GLM-5.2 Sparse on TPUs", section "Stream indexer scores over
+ * live context": the streaming indexer applies the masks and pools page
+ * maxima on chip, so only page scores reach HBM).
+ *
+ * Equal to dsa_indexer_scores followed by dsa_page_scores with the same
+ * page_size, and bit-identical to that pair where it runs (same arithmetic per
+ * token score). Arguments as for dsa_indexer_scores, plus page_size and the
+ * page_scores output of dsa_page_scores.
+ *
+ * Supported where the key stream runs in 64-key blocks: bf16 queries, head_dim
+ * 128, 16, 32 or 64 heads, bf16 or fp8 keys in pages of a multiple of 64 rows,
+ * fewer than 16 queries per sequence, and page_size 64 (one streamed block);
+ * otherwise DSA_ERR_UNSUPPORTED (the two-call route covers every case).
+ * Other errors as for the two calls.
+ */
+dsa_status dsa_indexer_page_scores(const dsa_batch *batch, const void *q_idx, int32_t q_dtype,
+                                   const float *w, int32_t n_heads, int32_t head_dim,
+                                   const dsa_paged_cache *keys, int32_t page_size,
+                                   float *page_scores, int64_t ld_pages, void *stream);
+
 /* Bytes of workspace dsa_page_topk needs for these host bounds (0 if none). */
 size_t dsa_page_topk_workspace_size(int32_t total_q, int32_t max_seq_len, int32_t page_size,
                                     int32_t kp);

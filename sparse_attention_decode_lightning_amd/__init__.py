@@ -30,7 +30,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "Batch", "PagedCache", "DSAError", "indexer_scores", "topk", "sparse_mla_fwd",
     "topk_workspace_size", "sparse_mla_workspace_size", "abi_version", "kv_append",
-    "page_scores", "page_topk", "page_topk_workspace_size",
+    "page_scores", "page_topk", "page_topk_workspace_size", "indexer_page_scores",
 ]
 
 _DT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.uint8: DSA_FP8_E4M3,
@@ -161,6 +161,30 @@ def page_scores(batch: Batch, scores: torch.Tensor, page_size: int,
     check(lib.dsa_page_scores(ctypes.byref(b), _dev(scores, "scores", torch.float32),
                               scores.shape[1], page_size, _dev(out, "page_scores", torch.float32),
                               out.shape[1], _stream(scores.device)), "dsa_page_scores")
+    return out
+
+
+def indexer_page_scores(batch: Batch, q_idx: torch.Tensor, w: torch.Tensor, keys: PagedCache,
+                        page_size: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """[T, ld_pages] fp32 page maxima of the indexer scores, computed without writing token
+    scores (the streamed-key configurations only; DSAError(UNSUPPORTED) otherwise)."""
+    T, H, D = q_idx.shape
+    qd = _DT.get(q_idx.dtype)
+    if qd not in (DSA_F32, DSA_BF16):
+        raise TypeError("q_idx must be float32 or bfloat16")
+    if tuple(w.shape) != (T, H):
+        raise ValueError("w must be [T, n_heads]")
+    n_pages = max(1, -(-batch.max_seq_len // page_size))
+    if out is None:
+        out = torch.empty((T, n_pages), dtype=torch.float32, device=q_idx.device)
+    if out.dim() != 2 or out.shape[0] != T:
+        raise ValueError("page scores must be [T, ld_pages]")
+    b, kc = batch.c(), keys.c()
+    check(lib.dsa_indexer_page_scores(ctypes.byref(b), _dev(q_idx, "q_idx"), qd,
+                                      _dev(w, "w", torch.float32), H, D, ctypes.byref(kc),
+                                      page_size, _dev(out, "page_scores", torch.float32),
+                                      out.shape[1], _stream(q_idx.device)),
+          "dsa_indexer_page_scores")
     return out
 
 

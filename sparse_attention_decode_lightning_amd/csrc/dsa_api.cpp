@@ -167,6 +167,31 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_d
                                               workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
+dsa_status dsa_indexer_page_scores(const dsa_batch *batch, const void *q_idx, int32_t q_dtype,
+                                   const float *w, int32_t n_heads, int32_t head_dim,
+                                   const dsa_paged_cache *keys, int32_t page_size,
+                                   float *page_scores, int64_t ld_pages, void *stream) {
+  BatchArgs bt;
+  CacheArgs kc;
+  dsa_status st = check_batch(batch, &bt);
+  if (st != DSA_OK) return st;
+  if (keys == nullptr || q_idx == nullptr || w == nullptr || page_scores == nullptr)
+    return DSA_ERR_NULL;
+  st = check_cache(keys, bt, &kc);
+  if (st != DSA_OK) return st;
+  if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (n_heads < 1 || head_dim < 1 || kc.row_elems != head_dim || page_size < 1)
+    return DSA_ERR_SHAPE;
+  if (ld_pages < dsa::candidate_bound(bt.max_seq_len, page_size) || ld_pages < 1)
+    return DSA_ERR_SHAPE;
+  if (!aligned(q_idx, 16) || !aligned(w, 4) || !aligned(page_scores, 4)) return DSA_ERR_SHAPE;
+  if (!dsa::indexer_page_max_supported(bt, q_dtype, n_heads, head_dim, kc, page_size))
+    return DSA_ERR_UNSUPPORTED;
+  return launch_status(dsa::launch_indexer_page_scores(bt, q_idx, w, n_heads, kc, page_size,
+                                                       page_scores, ld_pages,
+                                                       static_cast<hipStream_t>(stream)));
+}
+
 dsa_status dsa_page_scores(const dsa_batch *batch, const float *scores, int64_t ld_scores,
                            int32_t page_size, float *page_scores, int64_t ld_pages, void *stream) {
   BatchArgs bt;

@@ -38,6 +38,14 @@ hipError_t launch_indexer_scores(const BatchArgs &bt, const void *q_idx, int32_t
 // Top-k over candidates: positions (unit 1) or pages of `unit` positions;
 // sizes and support are in candidates per row (candidate_bound of the batch).
 int candidate_bound(int32_t max_seq_len, int32_t unit);
+// Page maxima straight from the indexer (selection pages of 64 positions;
+// bf16 queries of width 128; streamed key caches).
+bool indexer_page_max_supported(const BatchArgs &bt, int32_t q_dtype, int32_t n_heads,
+                                int32_t head_dim, const CacheArgs &keys, int32_t sel_page);
+hipError_t launch_indexer_page_scores(const BatchArgs &bt, const void *q_idx, const float *w,
+                                      int32_t n_heads, const CacheArgs &keys, int32_t sel_page,
+                                      float *page_scores, int64_t ld_pages, hipStream_t stream);
+
 size_t topk_workspace_bytes(int32_t total_q, int32_t max_cands, int32_t k);
 bool topk_supported(int32_t max_cands, int32_t k);
 hipError_t launch_topk(const BatchArgs &bt, const float *scores, int64_t ld_scores, int32_t k,

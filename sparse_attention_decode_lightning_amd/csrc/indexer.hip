@@ -190,13 +190,18 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-template <int NMT, int QG, bool FP8>
+// PMAX: instead of the token scores, each row's page maxima over logical
+// pages of one 64-key block (the selection's pages):
+// scores[row * ld + page] = max of the page's scores at positions <= t (pages
+// wholly past t are not written).
+template <int NMT, int QG, bool FP8, bool PMAX>
 __global__ __launch_bounds__(256) void indexer_stream_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ cu_q, int batch, int total_q, int max_seq_len, int64_t bt_stride,
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
     const uint8_t *__restrict__ kdata, const float *__restrict__ kscale, int64_t num_pages,
-    int page_size, FastDiv pdiv, float *__restrict__ scores, int64_t ld, int run_blocks) {
+    int page_size, FastDiv pdiv, float *__restrict__ scores, int64_t ld, int run_blocks,
+    int page_blocks) {
   constexpr int H = NMT * 16;
   constexpr int RB = FP8 ? kIdxDim : 2 * kIdxDim;    // bytes per key row
   constexpr int CPK = RB / 16;                      // 16-byte chunks per key
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
   __shared__ __attribute__((aligned(256))) float s_sc[kStreamStages][kStreamKeys];
   // scores of the workgroup's keys, written out after the loop so that the
   // only memory operations inside it are the direct copies
-  __shared__ float s_out[QG][kStreamBlocks * kStreamKeys];
+  __shared__ __attribute__((aligned(16))) float s_out[QG][kStreamBlocks * kStreamKeys];
 
   const int chunk = blockIdx.x, qgrp = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -339,12 +344,31 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
       lds_barrier();
       const int base = key0 + (blk - blk % kStreamBlocks) * kStreamKeys;  // first buffered key
       const int nbuf = (blk % kStreamBlocks + 1) * kStreamKeys;
+      if constexpr (!PMAX) {
 #pragma unroll
-      for (int qi = 0; qi < QG; ++qi) {
-        if (qi >= nq) break;
-        const int lim = min(nbuf, t_first + qi + 1 - base);  // causal: pos <= t
-        float *dst = scores + (int64_t)(q0 + i0 + qi) * ld + base;
-        for (int i = tid; i < lim; i += 256) dst[i] = s_out[qi][i];
+        for (int qi = 0; qi < QG; ++qi) {
+          if (qi >= nq) break;
+          const int lim = min(nbuf, t_first + qi + 1 - base);  // causal: pos <= t
+          float *dst = scores + (int64_t)(q0 + i0 + qi) * ld + base;
+          for (int i = tid; i < lim; i += 256) dst[i] = s_out[qi][i];
+        }
+      } else {
+        // pages of one 64-key block: thread tid takes keys 4 tid .. 4 tid + 3 of
+        // the buffer, 16 lanes make a page, whose maximum over positions <= t
+        // a DPP reduction gives to its first lane (the buffer starts on a page)
+        const int kk = 4 * tid;
+#pragma unroll
+        for (int qi = 0; qi < QG; ++qi) {
+          if (qi >= nq) break;
+          const int lim = min(nbuf, t_first + qi + 1 - base);  // causal: pos <= t
+          const f32x4_t v = *reinterpret_cast<const f32x4_t *>(&s_out[qi][kk]);
+          float m = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m = kk + e < lim ? fmaxf(m, v[e]) : m;
+          m = row16_max(m);
+          if ((lane & 15) == 0 && kk < lim)
+            scores[(int64_t)(q0 + i0 + qi) * ld + base / kStreamKeys + tid / 16] = m;
+        }
       }
       lds_barrier();
     }
@@ -664,9 +688,10 @@ hipError_t launch_prefill(const BatchArgs &bt, const void *q_idx, const float *w
   return hipGetLastError();
 }
 
-template <int NMT, int QG, bool FP8>
+template <int NMT, int QG, bool FP8, bool PMAX = false>
 hipError_t launch_stream(const BatchArgs &bt, const void *q_idx, const float *w,
-                         const CacheArgs &keys, float *scores, int64_t ld, hipStream_t stream) {
+                         const CacheArgs &keys, float *scores, int64_t ld, hipStream_t stream,
+                         int page_blocks = 1) {
   const int qgroups = (bt.max_q + QG - 1) / QG;
   const int64_t seq_blocks = (bt.max_seq_len + kStreamKeys - 1) / kStreamKeys;
   const int64_t units = (int64_t)qgroups * bt.batch;
@@ -680,11 +705,12 @@ hipError_t launch_stream(const BatchArgs &bt, const void *q_idx, const float *w,
   const int64_t chunks = (seq_blocks + run - 1) / run;
   if (qgroups > 65535 || bt.batch > 65535 || chunks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)chunks, qgroups, bt.batch);
-  hipLaunchKernelGGL((indexer_stream_kernel<NMT, QG, FP8>), grid, dim3(256), 0, stream,
+  hipLaunchKernelGGL((indexer_stream_kernel<NMT, QG, FP8, PMAX>), grid, dim3(256), 0, stream,
                      bt.block_table, bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len,
                      bt.bt_stride, static_cast<const uint16_t *>(q_idx), w,
                      static_cast<const uint8_t *>(keys.data), keys.scale, keys.num_pages,
-                     keys.page_size, make_fast_div((uint32_t)keys.page_size), scores, ld, (int)run);
+                     keys.page_size, make_fast_div((uint32_t)keys.page_size), scores, ld, (int)run,
+                     page_blocks);
   return hipGetLastError();
 }
 
@@ -727,6 +753,27 @@ hipError_t dispatch_mfma(const BatchArgs &bt, const void *q_idx, const float *w,
   }
 }
 
+// Page maxima straight from the streaming kernel (no token scores in HBM):
+// keys streamed in 64-key blocks and selection pages of one block.
+template <bool FP8>
+hipError_t dispatch_page_max(const BatchArgs &bt, const void *q_idx, const float *w, int n_heads,
+                             const CacheArgs &keys, int32_t sel_page, float *page_scores,
+                             int64_t ld_pages, hipStream_t stream) {
+  const int pb = sel_page / kStreamKeys;
+  const bool multi = bt.max_q > 1;
+  switch (n_heads) {
+    case 16:
+      return multi ? launch_stream<1, 4, FP8, true>(bt, q_idx, w, keys, page_scores, ld_pages, stream, pb)
+                   : launch_stream<1, 1, FP8, true>(bt, q_idx, w, keys, page_scores, ld_pages, stream, pb);
+    case 32:
+      return multi ? launch_stream<2, 4, FP8, true>(bt, q_idx, w, keys, page_scores, ld_pages, stream, pb)
+                   : launch_stream<2, 1, FP8, true>(bt, q_idx, w, keys, page_scores, ld_pages, stream, pb);
+    default:
+      return multi ? launch_stream<4, 2, FP8, true>(bt, q_idx, w, keys, page_scores, ld_pages, stream, pb)
+                   : launch_stream<4, 1, FP8, true>(bt, q_idx, w, keys, page_scores, ld_pages, stream, pb);
+  }
+}
+
 template <typename QT, int KDT>
 hipError_t launch_generic(const BatchArgs &bt, const void *q_idx, const float *w, int H, int D,
                           const CacheArgs &keys, float *scores, int64_t ld, hipStream_t stream) {
@@ -740,6 +787,26 @@ hipError_t launch_generic(const BatchArgs &bt, const void *q_idx, const float *w
 }
 
 }  // namespace
+
+bool indexer_page_max_supported(const BatchArgs &bt, int32_t q_dtype, int32_t n_heads,
+                                int32_t head_dim, const CacheArgs &keys, int32_t sel_page) {
+  const bool heads_ok = n_heads == 16 || n_heads == 32 || n_heads == 64;
+  const bool page_ok = sel_page == kStreamKeys;
+  return q_dtype == DSA_BF16 && head_dim == kIdxDim && heads_ok && page_ok &&
+         (keys.dtype == DSA_BF16 || keys.dtype == DSA_FP8_E4M3) &&
+         keys.page_size % kStreamKeys == 0 && bt.max_q < kPrefillMinQ;
+}
+
+hipError_t launch_indexer_page_scores(const BatchArgs &bt, const void *q_idx, const float *w,
+                                      int32_t n_heads, const CacheArgs &keys, int32_t sel_page,
+                                      float *page_scores, int64_t ld_pages, hipStream_t stream) {
+  if (bt.total_q == 0 || bt.max_seq_len == 0) return hipSuccess;
+  if (keys.dtype == DSA_FP8_E4M3)
+    return dispatch_page_max<true>(bt, q_idx, w, n_heads, keys, sel_page, page_scores, ld_pages,
+                                   stream);
+  return dispatch_page_max<false>(bt, q_idx, w, n_heads, keys, sel_page, page_scores, ld_pages,
+                                  stream);
+}
 
 hipError_t launch_indexer_scores(const BatchArgs &bt, const void *q_idx, int32_t q_dtype,
                                  const float *w, int32_t n_heads, int32_t head_dim,

@@ -103,3 +103,48 @@ def test_page_topk_rejects_bad_arguments():
         dsa.page_topk(b, ps, 16, 0)
     with pytest.raises(dsa.DSAError):  # ld_pages shorter than ceil(max_seq_len / page)
         dsa.page_topk(b, ps[:, :3], 16, 2)
+
+
+FUSED = [
+    # (base workload, overrides, selection page size)
+    ("decode_b32_l8k", dict(batch=3, lens=(1500, 700, 64), topk=256), 64),
+    ("decode_b32_l8k", dict(batch=3, lens=(5000, 1025, 130), topk=256), 64),
+    ("verify_b8_l240k", dict(batch=2, lens=(3000, 1100), topk=256), 64),
+    ("verify_b8_l240k", dict(batch=3, lens=(4100, 2049, 65), topk=256), 64),
+    ("decode_b32_l8k", dict(batch=2, lens=(900, 333), topk=256, idx_heads=64,
+                            w_std=0.125), 64),
+    ("decode_b32_l8k", dict(batch=2, lens=(1900, 333), topk=256, idx_heads=16,
+                            w_std=0.25, page_size=128), 64),
+]
+
+
+@pytest.mark.parametrize("base,kw,page", FUSED, ids=[f"{c[0]}-P{c[2]}" for c in FUSED])
+def test_fused_page_scores_equal_two_call_route(base, kw, page):
+    """dsa_indexer_page_scores writes exactly what dsa_indexer_scores + dsa_page_scores
+    write (same per-token arithmetic), and nothing past each row's last legal page."""
+    dsa = _dsa()
+    wl = small_variant(base, **kw)
+    inp = to_device(make_inputs(wl), torch.device("cuda:0"))
+    b = P.batch_of(inp)
+    n_pages = -(-inp.max_seq_len // page)
+    scores = _scores_with_poison(inp, dsa, b)
+    two = torch.full((inp.total_q, n_pages), float("nan"), device=scores.device)
+    dsa.page_scores(b, scores, page, out=two)
+    fused = torch.full((inp.total_q + 1, n_pages + 3), float("nan"), device=scores.device)
+    dsa.indexer_page_scores(b, inp.q_idx, inp.w, P.keys_of(inp), page,
+                            out=fused[: inp.total_q])
+    torch.cuda.synchronize()
+    assert torch.isnan(fused[inp.total_q]).all() and torch.isnan(fused[:, n_pages:]).all()
+    a, c = fused[: inp.total_q, :n_pages].cpu().numpy(), two.cpu().numpy()
+    assert np.array_equal(np.isnan(a), np.isnan(c))
+    assert np.array_equal(a[~np.isnan(a)].view(np.uint32), c[~np.isnan(c)].view(np.uint32))
+
+
+def test_fused_page_scores_unsupported_shapes():
+    dsa = _dsa()
+    wl = small_variant("decode_b32_l8k", batch=1, lens=(500,), topk=256)
+    inp = to_device(make_inputs(wl), torch.device("cuda:0"))
+    b = P.batch_of(inp)
+    for page in (16, 128, 1024):  # only pages of one streamed 64-key block
+        with pytest.raises(dsa.DSAError):
+            dsa.indexer_page_scores(b, inp.q_idx, inp.w, P.keys_of(inp), page)
