@@ -33,6 +33,9 @@ def _scores_with_poison(inp, dsa, b):
 
 CASES = [
     # (base workload, overrides, page size, page budget)
+    # the 4,096-token prefill budget of 32 pages of 128 ("Making GLM-5.2 Sparse on TPUs",
+    # section "Separate the indexer from the attention it controls"): k = 4096 in the MLA
+    ("decode_b32_l8k", dict(batch=2, lens=(6000, 4500), topk=256, page_size=128), 128, 32),
     ("decode_b32_l8k", dict(batch=3, lens=(1500, 700, 64), topk=256), 64, 8),
     ("verify_b8_l240k", dict(batch=2, lens=(3000, 1100), topk=256), 64, 5),
     ("decode_b32_l8k", dict(batch=2, lens=(2000, 513), topk=256, page_size=16), 16, 20),
