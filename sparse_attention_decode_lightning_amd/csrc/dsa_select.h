@@ -7,8 +7,10 @@
 // folded into +0.0 so the two compare equal. Scores map to order-preserving
 // 32-bit keys, so the order is (key descending, position ascending).
 //
-// A block of NW waves holds candidates u * (64 NW) + tid (u < R) as keys in
-// registers.
+// A block of NW waves holds candidates wave-major: wave w, slice u < R, lane
+// l holds candidate 64 R w + 64 u + l (sel_cand), so a slice is 64
+// consecutive candidates (one coalesced 256-byte load) and a wave's
+// candidates are one contiguous range.
 //  * Three radix levels (11, 11 and 10 bits) use three LDS histograms that are
 //    cleared before the first level, so a level costs one barrier: after it
 //    every wave scans the whole histogram itself and reaches the same digit.
@@ -19,11 +21,11 @@
 //    (its count equals what is still needed): the keys above the bin and all
 //    keys in it are then the top k. Continuous scores usually stop after two
 //    levels.
-//  * Ordered emit: positions run u-major, then wave, then lane, so per-u wave
-//    ballots of "above the bin" and "in the bin", one exclusive scan of the
-//    R x NW packed per-wave counts (done by every wave on its own) and a
-//    popcount below the lane give every kept candidate its slot in ascending
-//    position order, with no sort.
+//  * Ordered emit: each wave counts its keys above the bin and in it, one
+//    scan of the NW wave totals gives every wave its offsets, and inside the
+//    wave the slices are walked in order with running counts plus a popcount
+//    of the slice's ballot below the lane: every kept candidate gets its slot
+//    in ascending candidate order, with no sort.
 #pragma once
 
 #include "dsa_device.h"
@@ -107,14 +109,18 @@ __device__ __forceinline__ void wave_pick(const uint32_t *hist, uint32_t need, u
   rest = need - (above_l + s_i - h_i);
 }
 
-// LDS of one selection: the three histograms, the packed per-(u, wave)
-// counts and each wave's private copy of their exclusive scan.
+// LDS of one selection: the three histograms and the packed per-wave counts.
 template <int NW, int R>
 struct alignas(16) SelectShared {
   uint32_t hist[3][kSelBinsWords];
-  uint32_t cnt[R * NW];
-  uint32_t scan[NW][R * NW];
+  uint32_t cnt[NW];
 };
+
+// Candidate index held by slice u of the calling lane (wave-major layout).
+template <int R>
+__device__ __forceinline__ int sel_cand(int u) {
+  return (threadIdx.x >> 6) * (kWave * R) + u * kWave + (threadIdx.x & 63);
+}
 
 // Zero the histograms (no barrier: select_run starts with one).
 template <int NW, int R>
@@ -123,14 +129,24 @@ __device__ __forceinline__ void select_clear(SelectShared<NW, R> &sh) {
   for (int i = threadIdx.x; i < 3 * kSelBinsWords / 4; i += NW * kWave) h[i] = u32x4_t{0u, 0u, 0u, 0u};
 }
 
-// The k best of the n candidates u * (64 NW) + tid (< n, and n > k): emit(u,
-// slot) is called once for every kept candidate, with its slot in [0, k) of
-// the ascending-position list. Every thread of the block must call it.
+// The k best of the n candidates sel_cand(u) < n (n > k): emit(u, slot) is
+// called once for every kept candidate, with its slot in [0, k) of the
+// ascending-candidate list. Every thread of the block must call it.
 template <int NW, int R, typename Emit>
 __device__ __forceinline__ void select_run(const uint32_t (&key)[R], int n, int k,
                                            SelectShared<NW, R> &sh, Emit emit) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  auto valid = [&](int u) { return u * NW * kWave + tid < n; };
+  static_assert(NW * R * kWave < 65536, "16-bit packed counts");
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // candidates of this wave: slice u, lane l exists when l < n_w - 64 u
+  const int n_w = __builtin_amdgcn_readfirstlane(n) - wv * (kWave * R);
+  // (the bound passes through an empty asm so that each use compares afresh
+  // instead of keeping R lane masks live in scalar registers)
+  auto valid = [&](int u) {
+    int b = n_w - u * kWave;
+    asm volatile("" : "+s"(b));
+    return lane < b;
+  };
   __syncthreads();  // histograms cleared
 
   // level 1: bits 31..21
@@ -167,46 +183,37 @@ __device__ __forceinline__ void select_run(const uint32_t (&key)[R], int n, int 
   const uint32_t tp = prefix >> shift;
 
   // ordered emit: "above" = keys above the chosen bin, "in" = keys in it, of
-  // which the first `need` (by position) are kept
+  // which the first `need` (in candidate order) are kept. Wave totals,
+  // packed (above << 16 | in), then the exclusive sum over earlier waves.
+  uint32_t ngt = 0, neq = 0;
 #pragma unroll
   for (int u = 0; u < R; ++u) {
-    const uint64_t mg = __ballot(valid(u) && (key[u] >> shift) > tp);
-    const uint64_t me = __ballot(valid(u) && (key[u] >> shift) == tp);
-    if (lane == 0)
-      sh.cnt[u * NW + wv] = ((uint32_t)__popcll(mg) << 16) | (uint32_t)__popcll(me);
+    const uint32_t hd = key[u] >> shift;
+    ngt += (valid(u) && hd > tp) ? 1u : 0u;
+    neq += (valid(u) && hd == tp) ? 1u : 0u;
   }
+  const uint32_t wsum = wave_prefix_sum((ngt << 16) | neq);
+  if (lane == kWave - 1) sh.cnt[wv] = wsum;
   __syncthreads();
-  {
-    // exclusive scan of the R * NW packed counts in (u, wave) order, by every
-    // wave into its own copy
-    constexpr int per = (R * NW + 63) / 64;
-    uint32_t c[per], tot = 0;
-#pragma unroll
-    for (int i = 0; i < per; ++i) {
-      c[i] = per * lane + i < R * NW ? sh.cnt[per * lane + i] : 0u;
-      tot += c[i];
-    }
-    uint32_t run = wave_prefix_sum(tot) - tot;
-#pragma unroll
-    for (int i = 0; i < per; ++i) {
-      if (per * lane + i < R * NW) sh.scan[wv][per * lane + i] = run;
-      run += c[i];
-    }
-  }
-  const uint64_t below = (1ull << lane) - 1ull;
+  const uint32_t before = wave_prefix_sum(lane < wv ? sh.cnt[lane] : 0u);
+  uint32_t off = __builtin_amdgcn_readlane(before, kWave - 1);
+  uint32_t gt_run = off >> 16, eq_run = off & 0xFFFFu;
 #pragma unroll
   for (int u = 0; u < R; ++u) {
-    const uint32_t off = sh.scan[wv][u * NW + wv];
-    const bool gt = valid(u) && (key[u] >> shift) > tp;
-    const bool eq = valid(u) && (key[u] >> shift) == tp;
+    const uint32_t hd = key[u] >> shift;
+    const bool gt = valid(u) && hd > tp;
+    const bool eq = valid(u) && hd == tp;
     const uint64_t mg = __ballot(gt);
     const uint64_t me = __ballot(eq);
-    const uint32_t gt_before = (off >> 16) + (uint32_t)__popcll(mg & below);
-    const uint32_t eq_before = (off & 0xFFFFu) + (uint32_t)__popcll(me & below);
-    uint32_t slot = (uint32_t)k;
-    if (gt) slot = gt_before + min(eq_before, need);
-    else if (eq && eq_before < need) slot = gt_before + eq_before;
+    const uint32_t gt_before =
+        gt_run + __builtin_amdgcn_mbcnt_hi((uint32_t)(mg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mg, 0u));
+    const uint32_t eq_before =
+        eq_run + __builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u));
+    const uint32_t slot = gt ? gt_before + min(eq_before, need)
+                             : (eq && eq_before < need) ? gt_before + eq_before : (uint32_t)k;
     if (slot < (uint32_t)k) emit(u, (int)slot);
+    gt_run += (uint32_t)__popcll(mg);
+    eq_run += (uint32_t)__popcll(me);
   }
 }
 

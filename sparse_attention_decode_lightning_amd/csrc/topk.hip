@@ -323,14 +323,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
 constexpr int kRegThreads = 1024;
 
 // Rows of at most R * NT candidates (every row of up to 32K tokens):
-// NT threads, thread tid holding candidates u * NT + tid (u < R) as keys in
-// registers, selected by select_run (three pre-cleared LDS histograms, one
+// NT threads holding the candidates as keys in registers (slice u of lane l
+// of wave w: candidate sel_cand(u) = 64 R w + 64 u + l), selected by select_run (three pre-cleared LDS histograms, one
 // barrier per radix level, per-wave digit picks, an early stop once the chosen
 // bin is kept whole, a ballot-based ordered emit). The row's scores are
 // requested before its length is known (every load stays below
 // max_seq_len <= ld) and masked afterwards.
 template <int NT, int R>
-__global__ __launch_bounds__(NT) void topk_reg_kernel(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void topk_reg_kernel(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
     int total_q, int max_seq_len, int n_max, FastDiv unit, const float *__restrict__ scores,
     int64_t ld, int k,
@@ -339,13 +339,13 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(
   __shared__ SelectShared<NT / kWave, R> sh;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
-  const float *src = scores + (int64_t)row * ld;
+  const int lane = tid & 63;
+  const int w0 = __builtin_amdgcn_readfirstlane(tid >> 6) * (kWave * R);  // the wave's first candidate
+  const float *src = scores + (int64_t)row * ld + w0 + lane;
+  const int lim = n_max - w0;  // slice u of this lane is below n_max when lane < lim - 64 u
   float v[R];
 #pragma unroll
-  for (int u = 0; u < R; ++u) {
-    const int i = u * kRegThreads + tid;
-    v[u] = i < n_max ? src[i] : 0.0f;
-  }
+  for (int u = 0; u < R; ++u) v[u] = lane < lim - u * kWave ? src[u * kWave] : 0.0f;
   select_clear(sh);
   const int n = row_cands(cu_q, seq_lens, batch, total_q, max_seq_len, row, unit);
   int32_t *out = indices + (int64_t)row * k;
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(
   uint32_t key[R];
 #pragma unroll
   for (int u = 0; u < R; ++u) key[u] = order_key(v[u]);
-  select_run(key, n, k, sh, [&](int u, int slot) { out[slot] = u * kRegThreads + tid; });
+  select_run(key, n, k, sh, [&](int u, int slot) { out[slot] = sel_cand<R>(u); });
 }
 
 // Rows longer than one register block (32K): two phases on the same selection.
@@ -378,7 +378,7 @@ bool split_path(int32_t max_seq_len, int32_t k) {
   return max_seq_len > 32 * kRegThreads && (int64_t)split_chunks(max_seq_len) * k <= kSplitCands;
 }
 
-__global__ __launch_bounds__(kRegThreads) void topk_chunk_kernel(
+__global__ __launch_bounds__(kRegThreads) __attribute__((amdgpu_waves_per_eu(8))) void topk_chunk_kernel(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
     int total_q, int max_seq_len, int n_max, FastDiv unit, const float *__restrict__ scores,
     int64_t ld, int k, int nc,
@@ -388,13 +388,13 @@ __global__ __launch_bounds__(kRegThreads) void topk_chunk_kernel(
   const int c = blockIdx.x, row = blockIdx.y;
   const int tid = threadIdx.x;
   const int base = c * kSplitChunk;
-  const float *src = scores + (int64_t)row * ld + base;
+  const int lane = tid & 63;
+  const int w0 = __builtin_amdgcn_readfirstlane(tid >> 6) * (kWave * R);
+  const float *src = scores + (int64_t)row * ld + base + w0 + lane;
+  const int lim = n_max - base - w0;
   float v[R];
 #pragma unroll
-  for (int u = 0; u < R; ++u) {
-    const int i = u * kRegThreads + tid;
-    v[u] = base + i < n_max ? src[i] : 0.0f;
-  }
+  for (int u = 0; u < R; ++u) v[u] = lane < lim - u * kWave ? src[u * kWave] : 0.0f;
   select_clear(sh);
   const int n = row_cands(cu_q, seq_lens, batch, total_q, max_seq_len, row, unit);
   const int m = min(max(n - base, 0), kSplitChunk);  // candidates of this chunk
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_chunk_kernel(
   if (m <= k) {
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-      const int i = u * kRegThreads + tid;
+      const int i = sel_cand<R>(u);
       if (i < m) {
         okey[i] = key[u];
         opos[i] = base + i;
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_chunk_kernel(
   }
   select_run(key, m, k, sh, [&](int u, int slot) {
     okey[slot] = key[u];
-    opos[slot] = base + u * kRegThreads + tid;
+    opos[slot] = base + sel_cand<R>(u);
   });
 }
 
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_split_merge_kernel(
   int32_t pos[R];
 #pragma unroll
   for (int u = 0; u < R; ++u) {
-    const int j = u * kRegThreads + tid;
+    const int j = sel_cand<R>(u);
     const int c = (int)fast_div((uint32_t)j, kdiv);
     const int s = j - c * k;
     const int m = min(min(max(n - c * kSplitChunk, 0), kSplitChunk), k);  // survivors of chunk c
