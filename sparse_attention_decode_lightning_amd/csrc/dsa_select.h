@@ -34,6 +34,14 @@ namespace dsa {
 
 constexpr int kSelBins = 2048;                    // 11-bit digits
 constexpr int kSelBinsWords = kSelBins / 32 * 36;  // padded histogram
+// Levels 1 and 2 may count into C1 and C2 copies of their histograms, lane
+// l into copy l % copies, so lanes whose keys share a bin hit different
+// words; copies sit kSelCopyWords apart, 8 words past a multiple of the 32
+// banks, so the same bin of two copies is in different banks. This pays
+// where the keys crowd into few bins (the survivors of earlier selections);
+// on whole rows of scores the extra histogram reads cost more than the
+// spared conflicts.
+constexpr int kSelCopyWords = kSelBinsWords + 8;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -82,24 +90,31 @@ __device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v) {
 // serial search: lane totals of 32 (16) bins and their suffix sums find the
 // lane L whose bins hold the crossing; then lane i < 32 (16) reads bin
 // 32 L + i, and a second suffix sum and ballot find the bin.
-template <int NB>
+template <int NB, int C = 1>
 __device__ __forceinline__ void wave_pick(const uint32_t *hist, uint32_t need, uint32_t &digit,
                                           uint32_t &rest, uint32_t &count) {
   constexpr int per = NB / 64;
   const int lane = threadIdx.x & 63;
-  const u32x4_t *src = reinterpret_cast<const u32x4_t *>(hist + sel_bin(per * lane));
   uint32_t mine = 0;
 #pragma unroll
-  for (int i = 0; i < per / 4; ++i) {
-    const u32x4_t q = src[i];
-    mine += (q.x + q.y) + (q.z + q.w);
+  for (int c = 0; c < C; ++c) {
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(hist + c * kSelCopyWords + sel_bin(per * lane));
+#pragma unroll
+    for (int i = 0; i < per / 4; ++i) {
+      const u32x4_t q = src[i];
+      mine += (q.x + q.y) + (q.z + q.w);
+    }
   }
   const uint32_t suf = wave_suffix_sum(mine);
   const uint32_t above = suf - mine;
   const uint64_t who = __ballot(above < need && suf >= need);
   const int L = who != 0ull ? __ffsll((unsigned long long)who) - 1 : 0;
   const uint32_t above_l = __builtin_amdgcn_readlane(above, L);
-  const uint32_t hb = lane < per ? hist[sel_bin(per * L + lane)] : 0u;
+  uint32_t hb = 0;
+  if (lane < per) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) hb += hist[c * kSelCopyWords + sel_bin(per * L + lane)];
+  }
   const uint32_t s2 = wave_suffix_sum(hb);  // lanes >= per add 0
   const uint64_t hit = __ballot(lane < per && above_l + s2 >= need);
   const int i = hit != 0ull ? 63 - __clzll(hit) : 0;
@@ -110,9 +125,12 @@ __device__ __forceinline__ void wave_pick(const uint32_t *hist, uint32_t need, u
 }
 
 // LDS of one selection: the three histograms and the packed per-wave counts.
-template <int NW, int R>
+template <int NW, int R, int C1 = 1, int C2 = 1>
 struct alignas(16) SelectShared {
-  uint32_t hist[3][kSelBinsWords];
+  static constexpr int kCopies1 = C1, kCopies2 = C2;
+  uint32_t hist1[C1 * kSelCopyWords];
+  uint32_t hist2[C2 * kSelCopyWords];
+  uint32_t hist3[kSelBinsWords];
   uint32_t cnt[NW];
 };
 
@@ -123,18 +141,21 @@ __device__ __forceinline__ int sel_cand(int u) {
 }
 
 // Zero the histograms (no barrier: select_run starts with one).
-template <int NW, int R>
-__device__ __forceinline__ void select_clear(SelectShared<NW, R> &sh) {
-  u32x4_t *h = reinterpret_cast<u32x4_t *>(&sh.hist[0][0]);
-  for (int i = threadIdx.x; i < 3 * kSelBinsWords / 4; i += NW * kWave) h[i] = u32x4_t{0u, 0u, 0u, 0u};
+template <class Sh>
+__device__ __forceinline__ void select_clear(Sh &sh) {
+  constexpr int NW = sizeof(sh.cnt) / sizeof(uint32_t);
+  constexpr int kWords = (Sh::kCopies1 + Sh::kCopies2) * kSelCopyWords + kSelBinsWords;
+  static_assert(kWords % 4 == 0, "16-byte clears");
+  u32x4_t *h = reinterpret_cast<u32x4_t *>(&sh.hist1[0]);
+  for (int i = threadIdx.x; i < kWords / 4; i += NW * kWave) h[i] = u32x4_t{0u, 0u, 0u, 0u};
 }
 
 // The k best of the n candidates sel_cand(u) < n (n > k): emit(u, slot) is
 // called once for every kept candidate, with its slot in [0, k) of the
 // ascending-candidate list. Every thread of the block must call it.
-template <int NW, int R, typename Emit>
+template <int NW, int R, int C1, int C2, typename Emit>
 __device__ __forceinline__ void select_run(const uint32_t (&key)[R], int n, int k,
-                                           SelectShared<NW, R> &sh, Emit emit) {
+                                           SelectShared<NW, R, C1, C2> &sh, Emit emit) {
   static_assert(NW * R * kWave < 65536, "16-bit packed counts");
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -148,14 +169,16 @@ __device__ __forceinline__ void select_run(const uint32_t (&key)[R], int n, int 
     return lane < b;
   };
   __syncthreads();  // histograms cleared
+  uint32_t *h1 = sh.hist1 + (lane % C1) * kSelCopyWords;
+  uint32_t *h2 = sh.hist2 + (lane % C2) * kSelCopyWords;
 
   // level 1: bits 31..21
 #pragma unroll
   for (int u = 0; u < R; ++u)
-    if (valid(u)) atomicAdd(&sh.hist[0][sel_bin(key[u] >> 21)], 1u);
+    if (valid(u)) atomicAdd(&h1[sel_bin(key[u] >> 21)], 1u);
   __syncthreads();
   uint32_t d, need, count;
-  wave_pick<kSelBins>(sh.hist[0], (uint32_t)k, d, need, count);
+  wave_pick<kSelBins, C1>(sh.hist1, (uint32_t)k, d, need, count);
   uint32_t prefix = d << 21;
   int shift = 21;
   if (need != count) {
@@ -163,9 +186,9 @@ __device__ __forceinline__ void select_run(const uint32_t (&key)[R], int n, int 
 #pragma unroll
     for (int u = 0; u < R; ++u)
       if (valid(u) && (key[u] >> 21) == d)
-        atomicAdd(&sh.hist[1][sel_bin((key[u] >> 10) & 2047u)], 1u);
+        atomicAdd(&h2[sel_bin((key[u] >> 10) & 2047u)], 1u);
     __syncthreads();
-    wave_pick<kSelBins>(sh.hist[1], need, d, need, count);
+    wave_pick<kSelBins, C2>(sh.hist2, need, d, need, count);
     prefix |= d << 10;
     shift = 10;
     if (need != count) {
@@ -173,9 +196,9 @@ __device__ __forceinline__ void select_run(const uint32_t (&key)[R], int n, int 
 #pragma unroll
       for (int u = 0; u < R; ++u)
         if (valid(u) && (key[u] >> 10) == (prefix >> 10))
-          atomicAdd(&sh.hist[2][sel_bin(key[u] & 1023u)], 1u);
+          atomicAdd(&sh.hist3[sel_bin(key[u] & 1023u)], 1u);
       __syncthreads();
-      wave_pick<kSelBins / 2>(sh.hist[2], need, d, need, count);
+      wave_pick<kSelBins / 2>(sh.hist3, need, d, need, count);
       prefix |= d;
       shift = 0;
     }

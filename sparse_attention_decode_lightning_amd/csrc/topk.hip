@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kRegThreads) __attribute__((amdgpu_waves_per_eu(8))
     int64_t ld, int k, int nc,
     uint32_t *__restrict__ ws_key, int32_t *__restrict__ ws_pos) {
   constexpr int R = kSplitChunk / kRegThreads;
-  __shared__ SelectShared<kRegThreads / kWave, R> sh;
+  __shared__ SelectShared<kRegThreads / kWave, R, 4, 2> sh;
   const int c = blockIdx.x, row = blockIdx.y;
   const int tid = threadIdx.x;
   const int base = c * kSplitChunk;
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_split_merge_kernel(
     int total_q, int max_seq_len, int n_max, FastDiv unit, int k, FastDiv kdiv, int nc,
     const uint32_t *__restrict__ ws_key,
     const int32_t *__restrict__ ws_pos, int32_t *__restrict__ indices) {
-  __shared__ SelectShared<kRegThreads / kWave, R> sh;
+  __shared__ SelectShared<kRegThreads / kWave, R, 4, 2> sh;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   select_clear(sh);
