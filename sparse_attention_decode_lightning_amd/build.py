@@ -28,6 +28,10 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
+# Per-source extras: the indexer keeps its MFMA accumulators in ordinary
+# vector registers (its epilogue reads every accumulator element once, and
+# each read out of the accumulation registers costs a move).
+EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -39,7 +43,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [hipcc(), "-x", "hip", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), "-x", "hip", *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = ("unknown target feature", "packed-fp32-ops", "warning generated")
     err = "\n".join(ln for ln in r.stderr.splitlines() if not any(n in ln for n in noise))

@@ -318,26 +318,36 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
         bb[s_] = *(const __attribute__((address_space(3))) u32x4_t *)(st + kr * RB + 16 * swz(4 * s_ + g, kr));
     }
     const float ksc = FP8 ? *(const __attribute__((address_space(3))) float *)((const lds_u8 *)s_sc[blk % kStreamStages] + 4 * kr) : 1.0f;
-    const int pos = tile0 + j;
+    // every MFMA of the block first, then the epilogues, with no branch
+    // between them: the ReLU and weight work of one (query, head tile) then
+    // issues under the MFMAs of the next
+    f32x4_t acc[QG][NMT];
+#pragma unroll
+    for (int qi = 0; qi < QG; ++qi)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        acc[qi][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s_ = 0; s_ < 4; ++s_) acc[qi][mt] = mfma_16x16x32_bf16(a[qi][mt][s_], bb[s_], acc[qi][mt]);
+      }
+    float mine = 0.0f;  // lane group g keeps query g % QG
 #pragma unroll
     for (int qi = 0; qi < QG; ++qi) {
       float p = 0.0f;
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-        for (int s_ = 0; s_ < 4; ++s_) acc = mfma_16x16x32_bf16(a[qi][mt][s_], bb[s_], acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p = fmaf(wr[qi][mt][r], relu_bits(acc[r]), p);
-      }
+        for (int r = 0; r < 4; ++r) p = fmaf(wr[qi][mt][r], relu_bits(acc[qi][mt][r]), p);
       // head sum over the four lane groups; the positive per-key scale of
       // e4m3 keys factors out of the ReLU
       auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(p), false, false);
       p = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
       auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
       p = (__uint_as_float(s32[0]) + __uint_as_float(s32[1])) * ksc;
-      if ((qi & 3) == g) s_out[qi][(blk % kStreamBlocks) * kStreamKeys + 16 * wv + j] = p;
+      mine = (g % QG == qi) ? p : mine;
     }
+    // (lanes of groups that keep the same query store the same value)
+    s_out[g % QG][(blk % kStreamBlocks) * kStreamKeys + 16 * wv + j] = mine;
     }
     // every kStreamBlocks blocks (and at the end) write the buffered scores out
     if (blk % kStreamBlocks == kStreamBlocks - 1 || blk == nblk - 1) {
