@@ -25,6 +25,13 @@ namespace dsa {
 namespace {
 
 constexpr int kIdxDim = 128;
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16_bf16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
 constexpr int kIdxThreads = 256;
 constexpr int kIdxWaves = kIdxThreads / kWave;
 constexpr int kTilesPerWave = 4;
@@ -230,19 +237,43 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
   if (t_last < 0 || key0 > t_last) return;
   const int nblk = min(run_blocks, (t_last - key0) / kStreamKeys + 1);
 
-  // Query fragments: lane (g, j) holds head 16 mt + j, dims dim_of(s, g).
-  u32x4_t a[QG][NMT][4];
-  float wr[QG][NMT][4];
+  // Four query rows of 32 heads (draft verification) take the wide path:
+  // wave wv computes query rows 2 (wv >> 1) + {0, 1} against keys
+  // 32 (wv & 1) .. + 31 of a block on v_mfma_f32_32x32x16_bf16 (M = the 32
+  // heads of a row, N = 32 keys, 8 K-steps), whose 32-cycle MFMAs leave room
+  // for the ReLU and weight work of the other row. Lane (h, n): head or key
+  // n, dims 64 h + 8 s .. + 8 at step s on both operands; accumulator
+  // element 4 i + r is head 8 i + 4 h + r.
+  constexpr bool kWide = QG == 4 && NMT == 2;
+  const int wn = lane & 31, wh = lane >> 5;
+  constexpr int kA = kWide ? 1 : QG, kM = kWide ? 1 : NMT;
+  u32x4_t a[kA][kM][4];
+  float wr[kA][kM][4];
+  u32x4_t a2[kWide ? 2 : 1][8];
+  float w2[kWide ? 2 : 1][16];
+  if constexpr (kWide) {
 #pragma unroll
-  for (int qi = 0; qi < QG; ++qi) {
-    const int64_t row = q0 + i0 + min(qi, nq - 1);
+    for (int qq = 0; qq < 2; ++qq) {
+      const int64_t row = q0 + i0 + min(2 * (wv >> 1) + qq, nq - 1);
+      const uint16_t *qp = q_idx + (row * H + wn) * kIdxDim + 64 * wh;
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-      const uint16_t *qp = q_idx + (row * H + mt * 16 + j) * kIdxDim;
+      for (int s_ = 0; s_ < 8; ++s_) a2[qq][s_] = ldg16(qp + 8 * s_);
 #pragma unroll
-      for (int s_ = 0; s_ < 4; ++s_) a[qi][mt][s_] = ldg16(qp + dim_of<FP8>(s_, g));
+      for (int e = 0; e < 16; ++e) w2[qq][e] = w[row * H + 8 * (e >> 2) + 4 * wh + (e & 3)];
+    }
+  } else {
+    // Query fragments: lane (g, j) holds head 16 mt + j, dims dim_of(s, g).
 #pragma unroll
-      for (int r = 0; r < 4; ++r) wr[qi][mt][r] = w[row * H + mt * 16 + 4 * g + r];
+    for (int qi = 0; qi < QG; ++qi) {
+      const int64_t row = q0 + i0 + min(qi, nq - 1);
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const uint16_t *qp = q_idx + (row * H + mt * 16 + j) * kIdxDim;
+#pragma unroll
+        for (int s_ = 0; s_ < 4; ++s_) a[qi][mt][s_] = ldg16(qp + dim_of<FP8>(s_, g));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wr[qi][mt][r] = w[row * H + mt * 16 + 4 * g + r];
+      }
     }
   }
   // Copy map: wave wv's copy i of a block moves stage chunks 64 (4 i + wv) + l,
@@ -295,6 +326,65 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if (blk + kStreamStages - 1 < nblk) copy_block(blk + kStreamStages - 1);
 
+    if constexpr (kWide) {
+    const int kr = 32 * (wv & 1) + wn;  // key of this lane within the block
+    if (key0 + blk * kStreamKeys + 32 * (wv & 1) <= t_last) {
+    const lds_u8 *st = (const lds_u8 *)s_st[blk % kStreamStages];
+    u32x4_t bq[8];
+    if constexpr (FP8) {
+      // bytes 64 h .. 64 h + 63 of the key: four chunks of two K-steps each
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const u32x4_t src = *(const __attribute__((address_space(3))) u32x4_t *)(
+            st + kr * RB + 16 * swz(4 * wh + t, kr));
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const u32x2_t lo = e4m3x4_to_bf16x4(e ? src.z : src.x);
+          const u32x2_t hi = e4m3x4_to_bf16x4(e ? src.w : src.y);
+          bq[2 * t + e] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s_ = 0; s_ < 8; ++s_)
+        bq[s_] = *(const __attribute__((address_space(3))) u32x4_t *)(st + kr * RB + 16 * swz(8 * wh + s_, kr));
+    }
+    const float ksc = FP8 ? *(const __attribute__((address_space(3))) float *)((const lds_u8 *)s_sc[blk % kStreamStages] + 4 * kr) : 1.0f;
+    // row 0's MFMAs (the key conversions go in between), then row 1's, each
+    // followed by the ReLU and weight work of two of row 0's accumulator
+    // elements: the 32-cycle MFMAs hide that work
+    f32x16_t acc0, acc1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      acc0[e] = 0.0f;
+      acc1[e] = 0.0f;
+    }
+#pragma unroll
+    for (int s_ = 0; s_ < 8; ++s_) acc0 = mfma_32x32x16_bf16(a2[0][s_], bq[s_], acc0);
+    float p0 = 0.0f, p1 = 0.0f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s_ = 0; s_ < 8; ++s_) {
+      acc1 = mfma_32x32x16_bf16(a2[1][s_], bq[s_], acc1);
+      p0 = fmaf(w2[0][2 * s_], relu_bits(acc0[2 * s_]), p0);
+      p0 = fmaf(w2[0][2 * s_ + 1], relu_bits(acc0[2 * s_ + 1]), p0);
+      asm volatile("" : "+v"(p0));  // keeps the two steps here, not sunk to the end
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) p1 = fmaf(w2[1][e], relu_bits(acc1[e]), p1);
+    // lanes n and n + 32 hold the two halves of a row's head sum
+    float pt[2];
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const float p = qq ? p1 : p0;
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+      pt[qq] = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * ksc;
+    }
+    // half h of the wave stores query row 2 (wv >> 1) + h
+    s_out[2 * (wv >> 1) + wh][(blk % kStreamBlocks) * kStreamKeys + kr] = wh ? pt[1] : pt[0];
+    }
+    } else {
     const int tile0 = key0 + blk * kStreamKeys + 16 * wv;
     if (tile0 <= t_last) {
     const lds_u8 *st = (const lds_u8 *)s_st[blk % kStreamStages];
@@ -348,6 +438,7 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
     }
     // (lanes of groups that keep the same query store the same value)
     s_out[g % QG][(blk % kStreamBlocks) * kStreamKeys + 16 * wv + j] = mine;
+    }
     }
     // every kStreamBlocks blocks (and at the end) write the buffered scores out
     if (blk % kStreamBlocks == kStreamBlocks - 1 || blk == nblk - 1) {
@@ -411,12 +502,6 @@ constexpr int kPfKeys = 64;                              // keys per LDS block
 constexpr int kPfChunks = kPfKeys * kIdxDim * 2 / 16;    // 16-byte chunks per block
 constexpr int kPfStage = kPfChunks / kPfThreads;         // staged chunks per thread
 
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ f32x16_t mfma_32x32x16_bf16(u32x4_t a, u32x4_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
 
 // CONTIG: the page size is a multiple of kPfKeys, so each block of 64 keys is
 // 64 consecutive rows of one page, found with one (scalar) block-table read.

@@ -40,6 +40,11 @@ SMALL_CASES = {
     "idx64_heads": small_variant(BF16_DECODE, batch=2, lens=(500, 260), idx_heads=64, topk=128),
     "idx16_heads_multiq": small_variant("verify_b8_l240k", batch=2, lens=(400, 90), q_per_seq=5,
                                         idx_heads=16, topk=64),
+    # four query rows of 32 heads with bf16 keys (the 32x32 MFMA path of the
+    # streaming indexer), one group short of four rows, one sequence shorter
+    # than a block
+    "bf16_multiquery_h32": small_variant(BF16_DECODE, batch=3, lens=(700, 300, 40),
+                                         q_per_seq=(4, 3, 4), topk=128),
     "topk_two_phase": small_variant("indexshare_b64", batch=4, lens=(70000, 33000, 5000, 300),
                                     topk=512, n_layers=1),
     "mla_generic_bf16": small_variant(BF16_DECODE, batch=2, lens=(300, 129), mla_heads=16,
