@@ -161,11 +161,11 @@ __device__ __forceinline__ void select_run(const uint32_t (&key)[R], int n, int 
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // candidates of this wave: slice u, lane l exists when l < n_w - 64 u
   const int n_w = __builtin_amdgcn_readfirstlane(n) - wv * (kWave * R);
-  // (the bound passes through an empty asm so that each use compares afresh
-  // instead of keeping R lane masks live in scalar registers)
+  // (with 32 slices the bound passes through an empty asm, so that each use
+  // compares afresh instead of keeping R lane masks live in scalar registers)
   auto valid = [&](int u) {
     int b = n_w - u * kWave;
-    asm volatile("" : "+s"(b));
+    if constexpr (R >= 32) asm volatile("" : "+s"(b));
     return lane < b;
   };
   __syncthreads();  // histograms cleared
@@ -212,8 +212,9 @@ __device__ __forceinline__ void select_run(const uint32_t (&key)[R], int n, int 
 #pragma unroll
   for (int u = 0; u < R; ++u) {
     const uint32_t hd = key[u] >> shift;
-    ngt += (valid(u) && hd > tp) ? 1u : 0u;
-    neq += (valid(u) && hd == tp) ? 1u : 0u;
+    const bool vu = valid(u);
+    ngt += (vu && hd > tp) ? 1u : 0u;
+    neq += (vu && hd == tp) ? 1u : 0u;
   }
   const uint32_t wsum = wave_prefix_sum((ngt << 16) | neq);
   if (lane == kWave - 1) sh.cnt[wv] = wsum;
@@ -224,8 +225,9 @@ __device__ __forceinline__ void select_run(const uint32_t (&key)[R], int n, int 
 #pragma unroll
   for (int u = 0; u < R; ++u) {
     const uint32_t hd = key[u] >> shift;
-    const bool gt = valid(u) && hd > tp;
-    const bool eq = valid(u) && hd == tp;
+    const bool vu = valid(u);
+    const bool gt = vu && hd > tp;
+    const bool eq = vu && hd == tp;
     const uint64_t mg = __ballot(gt);
     const uint64_t me = __ballot(eq);
     const uint32_t gt_before =
