@@ -35,6 +35,10 @@
  * - Errors are status codes. All host-visible arguments are validated before
  *   anything is enqueued; on an error nothing is enqueued and no output is
  *   touched. No call aborts or throws across the ABI.
+ * - An empty batch (total_q = 0) is valid: the call checks its arguments,
+ *   enqueues nothing and returns DSA_OK; its per-row arrays (queries,
+ *   weights, scores, indices, pages, outputs) and the batch's metadata
+ *   arrays may then be NULL.
  * - Device-resident metadata (lengths, block tables, indices) is trusted to
  *   be in range, but clamped so that malformed values never make a kernel
  *   read or write outside the buffers described here: page ids are clamped
@@ -134,8 +138,8 @@ int32_t dsa_abi_version(void);
  *           F32 queries need F32 keys
  *   scores  device [total_q, ld_scores] fp32 output; ld_scores >= max_seq_len
  *
- * Errors: DSA_ERR_NULL for a NULL batch, keys, q_idx, w, scores, key data,
- * fp8 scale, or (with total_q > 0) NULL metadata arrays; DSA_ERR_SHAPE for
+ * Errors: DSA_ERR_NULL for a NULL batch, keys, key data or fp8 scale, or
+ * (with total_q > 0) a NULL q_idx, w, scores or metadata array; DSA_ERR_SHAPE for
  * non-positive heads/dims/page size, row_elems != head_dim, ld_scores <
  * max_seq_len, or inconsistent batch bounds; DSA_ERR_DTYPE for unsupported
  * element types; DSA_ERR_LAUNCH if the runtime rejects the launch.
@@ -199,8 +203,9 @@ size_t dsa_sparse_mla_workspace_size(int32_t total_q, int32_t n_heads, int32_t d
  *   lse      device [total_q, n_heads] fp32 output, or NULL
  *   workspace device, >= dsa_sparse_mla_workspace_size(total_q, n_heads, d_latent, k)
  *
- * Errors: DSA_ERR_NULL (including a NULL `indices`: a layer that has neither
- * its own nor a shared top-k buffer is rejected), DSA_ERR_SHAPE, DSA_ERR_DTYPE,
+ * Errors: DSA_ERR_NULL (a NULL kv, or with total_q > 0 a NULL q, out or
+ * `indices`: a layer that has neither its own nor a shared top-k buffer is
+ * rejected), DSA_ERR_SHAPE, DSA_ERR_DTYPE,
  * DSA_ERR_WORKSPACE, DSA_ERR_LAUNCH.
  */
 dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_dtype,

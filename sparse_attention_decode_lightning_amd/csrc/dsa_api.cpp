@@ -96,7 +96,8 @@ dsa_status dsa_indexer_scores(const dsa_batch *batch, const void *q_idx, int32_t
   CacheArgs kc;
   dsa_status st = check_batch(batch, &bt);
   if (st != DSA_OK) return st;
-  if (keys == nullptr || q_idx == nullptr || w == nullptr || scores == nullptr) return DSA_ERR_NULL;
+  if (keys == nullptr) return DSA_ERR_NULL;
+  if (bt.total_q > 0 && (q_idx == nullptr || w == nullptr || scores == nullptr)) return DSA_ERR_NULL;
   st = check_cache(keys, bt, &kc);
   if (st != DSA_OK) return st;
   if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
@@ -105,6 +106,7 @@ dsa_status dsa_indexer_scores(const dsa_batch *batch, const void *q_idx, int32_t
   if (n_heads < 1 || head_dim < 1 || kc.row_elems != head_dim) return DSA_ERR_SHAPE;
   if (ld_scores < bt.max_seq_len || ld_scores < 1) return DSA_ERR_SHAPE;
   if (!aligned(q_idx, 16) || !aligned(w, 4) || !aligned(scores, 4)) return DSA_ERR_SHAPE;
+  if (bt.total_q == 0) return DSA_OK;
   return launch_status(dsa::launch_indexer_scores(bt, q_idx, q_dtype, w, n_heads, head_dim, kc,
                                                   scores, ld_scores,
                                                   static_cast<hipStream_t>(stream)));
@@ -119,13 +121,14 @@ dsa_status dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld_scor
   BatchArgs bt;
   dsa_status st = check_batch(batch, &bt);
   if (st != DSA_OK) return st;
-  if (scores == nullptr || indices == nullptr) return DSA_ERR_NULL;
+  if (bt.total_q > 0 && (scores == nullptr || indices == nullptr)) return DSA_ERR_NULL;
   if (k < 1 || ld_scores < bt.max_seq_len || ld_scores < 1) return DSA_ERR_SHAPE;
   if (!aligned(scores, 4) || !aligned(indices, 4)) return DSA_ERR_SHAPE;
   if (!dsa::topk_supported(bt.max_seq_len, k)) return DSA_ERR_UNSUPPORTED;
   const size_t need = dsa::topk_workspace_bytes(bt.total_q, bt.max_seq_len, k);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
     return DSA_ERR_WORKSPACE;
+  if (bt.total_q == 0) return DSA_OK;
   return launch_status(dsa::launch_topk(bt, scores, ld_scores, k, 1, indices, workspace,
                                         workspace_bytes, static_cast<hipStream_t>(stream)));
 }
@@ -145,7 +148,8 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_d
   CacheArgs kc;
   dsa_status st = check_batch(batch, &bt);
   if (st != DSA_OK) return st;
-  if (kv == nullptr || q == nullptr || indices == nullptr || out == nullptr) return DSA_ERR_NULL;
+  if (kv == nullptr) return DSA_ERR_NULL;
+  if (bt.total_q > 0 && (q == nullptr || indices == nullptr || out == nullptr)) return DSA_ERR_NULL;
   st = check_cache(kv, bt, &kc);
   if (st != DSA_OK) return st;
   if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
@@ -162,6 +166,7 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_d
   const size_t need = dsa::mla_workspace_bytes(bt.total_q, n_heads, d_latent, k);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
     return DSA_ERR_WORKSPACE;
+  if (bt.total_q == 0) return DSA_OK;
   return launch_status(dsa::launch_sparse_mla(bt, q, q_dtype, n_heads, d_latent, d_rope, kc,
                                               indices, k, scale, out, lse, workspace,
                                               workspace_bytes, static_cast<hipStream_t>(stream)));
@@ -175,7 +180,8 @@ dsa_status dsa_indexer_page_scores(const dsa_batch *batch, const void *q_idx, in
   CacheArgs kc;
   dsa_status st = check_batch(batch, &bt);
   if (st != DSA_OK) return st;
-  if (keys == nullptr || q_idx == nullptr || w == nullptr || page_scores == nullptr)
+  if (keys == nullptr) return DSA_ERR_NULL;
+  if (bt.total_q > 0 && (q_idx == nullptr || w == nullptr || page_scores == nullptr))
     return DSA_ERR_NULL;
   st = check_cache(keys, bt, &kc);
   if (st != DSA_OK) return st;
@@ -187,6 +193,7 @@ dsa_status dsa_indexer_page_scores(const dsa_batch *batch, const void *q_idx, in
   if (!aligned(q_idx, 16) || !aligned(w, 4) || !aligned(page_scores, 4)) return DSA_ERR_SHAPE;
   if (!dsa::indexer_page_max_supported(bt, q_dtype, n_heads, head_dim, kc, page_size))
     return DSA_ERR_UNSUPPORTED;
+  if (bt.total_q == 0) return DSA_OK;
   return launch_status(dsa::launch_indexer_page_scores(bt, q_idx, w, n_heads, kc, page_size,
                                                        page_scores, ld_pages,
                                                        static_cast<hipStream_t>(stream)));
@@ -197,11 +204,12 @@ dsa_status dsa_page_scores(const dsa_batch *batch, const float *scores, int64_t 
   BatchArgs bt;
   const dsa_status st = check_batch(batch, &bt);
   if (st != DSA_OK) return st;
-  if (scores == nullptr || page_scores == nullptr) return DSA_ERR_NULL;
+  if (bt.total_q > 0 && (scores == nullptr || page_scores == nullptr)) return DSA_ERR_NULL;
   if (page_size < 1 || ld_scores < bt.max_seq_len || ld_scores < 1) return DSA_ERR_SHAPE;
   if (ld_pages < dsa::candidate_bound(bt.max_seq_len, page_size) || ld_pages < 1)
     return DSA_ERR_SHAPE;
   if (!aligned(scores, 4) || !aligned(page_scores, 4)) return DSA_ERR_SHAPE;
+  if (bt.total_q == 0) return DSA_OK;
   return launch_status(dsa::launch_page_scores(bt, scores, ld_scores, page_size, page_scores,
                                                ld_pages, static_cast<hipStream_t>(stream)));
 }
@@ -218,7 +226,7 @@ dsa_status dsa_page_topk(const dsa_batch *batch, const float *page_scores, int64
   BatchArgs bt;
   const dsa_status st = check_batch(batch, &bt);
   if (st != DSA_OK) return st;
-  if (page_scores == nullptr || pages == nullptr) return DSA_ERR_NULL;
+  if (bt.total_q > 0 && (page_scores == nullptr || pages == nullptr)) return DSA_ERR_NULL;
   if (page_size < 1 || kp < 1) return DSA_ERR_SHAPE;
   const int32_t max_pages = dsa::candidate_bound(bt.max_seq_len, page_size);
   if (ld_pages < max_pages || ld_pages < 1) return DSA_ERR_SHAPE;
@@ -229,6 +237,7 @@ dsa_status dsa_page_topk(const dsa_batch *batch, const float *page_scores, int64
   const size_t need = dsa::topk_workspace_bytes(bt.total_q, max_pages, kp);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
     return DSA_ERR_WORKSPACE;
+  if (bt.total_q == 0) return DSA_OK;
   return launch_status(dsa::launch_page_topk(bt, page_scores, ld_pages, page_size, kp, pages,
                                              indices, workspace, workspace_bytes,
                                              static_cast<hipStream_t>(stream)));

@@ -170,3 +170,26 @@ def test_kv_append_rejects_bad_arguments(kw, code):
 
 def test_kv_append_empty_is_a_no_op():
     assert _append(n=0, slots=0, lat=0, keys=0) == 0
+
+
+def test_empty_batch_is_a_validated_no_op():
+    """total_q = 0: nothing to enqueue, so per-row arrays and the batch's metadata
+    may be NULL; the remaining arguments are still checked."""
+    b = L.DsaBatch(block_table=None, seq_lens=None, cu_q=None, batch=0, bt_stride=0, total_q=0,
+                   max_seq_len=0, max_q=0)
+    kc = _cache()
+    assert _idx(b=b, q=None, w=None, s=None, ld=1) == 0
+    assert _topk(b=b, s=None, idx=None, ld=1) == 0
+    assert _mla(b=b, q=None, idx=None, out=None, lse=None, ws=None, wsb=0) == 0
+    assert L.lib.dsa_page_scores(ctypes.byref(b), None, 1, 64, None, 1, None) == 0
+    assert L.lib.dsa_page_topk(ctypes.byref(b), None, 1, 64, 32, None, None, None, 0, None) == 0
+    assert L.lib.dsa_indexer_page_scores(ctypes.byref(b), None, L.DSA_BF16, None, 32, 128,
+                                         ctypes.byref(kc), 64, None, 1, None) == 0
+    # still validated: strides, k, caches, element types
+    assert _idx(b=b, q=None, w=None, s=None, ld=0) == 2
+    assert _topk(b=b, s=None, idx=None, ld=1, k=0) == 2
+    assert _mla(b=b, c=False, q=None, idx=None, out=None) == 1
+    assert _mla(b=b, qd=L.DSA_F32, q=None, idx=None, out=None) == 3
+    assert L.lib.dsa_page_topk(ctypes.byref(b), None, 1, 64, 0, None, None, None, 0, None) == 2
+    # with queries, the same NULL arrays are errors
+    assert _idx(q=None) == 1 and _topk(idx=None) == 1 and _mla(out=None) == 1
