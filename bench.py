@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=WORKLOAD_DEFAULT)
     ap.add_argument("--no-flush", action="store_true", help="skip the cache eviction between steps")
+    ap.add_argument("--mla-per-layer", action="store_true",
+                    help="with several IndexShare layers: one dsa_sparse_mla_fwd call per layer "
+                         "instead of one dsa_sparse_mla_fwd_layers call for all of them")
     ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=False,
                     help="replay the step as a captured HIP graph instead of eager launches")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -343,7 +346,10 @@ def main():
             for _ in range(wl.n_layers)]
     lses = [torch.empty((T, wl.mla_heads), dtype=torch.float32, device=dev)
             for _ in range(wl.n_layers)]
-    ws_bytes = dsa.sparse_mla_workspace_size(T, wl.mla_heads, wl.d_latent, k_sel)
+    layered = wl.n_layers > 1 and not args.mla_per_layer
+    ws_bytes = (dsa.sparse_mla_layers_workspace_size(wl.n_layers, T, wl.mla_heads, wl.d_latent,
+                                                     k_sel) if layered else
+                dsa.sparse_mla_workspace_size(T, wl.mla_heads, wl.d_latent, k_sel))
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     tk_bytes = dsa.topk_workspace_size(T, inp.max_seq_len, wl.topk)
     tk_ws = torch.empty(max(tk_bytes, 16), dtype=torch.uint8, device=dev) if tk_bytes else None
@@ -359,7 +365,8 @@ def main():
         except dsa.DSAError:
             fused = False
     sel_names = (["page_topk"] if fused else ["page_scores", "page_topk"]) if kp else ["topk"]
-    n_ev = 2 + len(sel_names) + wl.n_layers
+    mla_calls = 1 if layered else wl.n_layers
+    n_ev = 2 + len(sel_names) + mla_calls
 
     def step(evs=None):
         e = 0
@@ -385,6 +392,13 @@ def main():
         e += 1
         if evs is not None:
             evs[e].record(stream)
+        if layered:
+            dsa.sparse_mla_fwd_layers(batch, inp.q_mla, kvs, indices, wl.d_latent, wl.scale,
+                                      outs=outs, lses=lses, workspace=ws)
+            e += 1
+            if evs is not None:
+                evs[e].record(stream)
+            return
         for l in range(wl.n_layers):
             dsa.sparse_mla_fwd(batch, inp.q_mla[l], kvs[l], indices, wl.d_latent, wl.scale,
                                out=outs[l], lse=lses[l], workspace=ws)
@@ -453,16 +467,19 @@ def main():
     warm_ms = w0.elapsed_time(w1) / args.steps
 
     ab = algorithmic_bytes(inp, k_sel=k_sel, page=page if kp else 0, fused=fused)
-    names = ["indexer"] + sel_names + [f"mla_l{l}" for l in range(wl.n_layers)]
+    names = ["indexer"] + sel_names + ([f"mla_{wl.n_layers}_layers"] if layered else
+                                       [f"mla_l{l}" for l in range(wl.n_layers)])
     n_sel = len(sel_names)
     mla_ms = float(np.sum(stage_ms[1 + n_sel:]))
     sel_ms = float(np.sum(stage_ms[1:1 + n_sel]))
     kern = {"indexer": (float(stage_ms[0]), ab["indexer"], "dsa_indexer_scores",
                         ab["flops_indexer"]),
             "topk": (sel_ms, ab["topk"], "dsa_page_topk" if kp else "dsa_topk", 0),
-            "sparse_mla": (mla_ms / wl.n_layers, ab["mla_per_layer"], "dsa_sparse_mla_fwd",
-                           ab["flops_mla_per_layer"])}
-    dom = max(kern, key=lambda k: kern[k][0] * (wl.n_layers if k == "sparse_mla" else 1))
+            # one call: one layer, or every layer through dsa_sparse_mla_fwd_layers
+            "sparse_mla": (mla_ms / mla_calls, ab["mla_per_layer"] * (wl.n_layers // mla_calls),
+                           "dsa_sparse_mla_fwd_layers" if layered else "dsa_sparse_mla_fwd",
+                           ab["flops_mla_per_layer"] * (wl.n_layers // mla_calls))}
+    dom = max(kern, key=lambda k: kern[k][0] * (mla_calls if k == "sparse_mla" else 1))
     d_ms, d_bytes, d_sym, d_flops = kern[dom]
     # the dominant call against the roofline it is closer to: HBM bytes or bf16 MFMA flops
     hbm_gbs = d_bytes / (d_ms * 1e-3) / 1e9

@@ -215,6 +215,38 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_d
                               size_t workspace_bytes, void *stream);
 
 /*
+ * IndexShare over several layers in one call ("GLM-5.2 on vLLM Ascend:
+ * Request-to-Backend Inference Path", section 7: one indexer's top-k is
+ * reused by the attention of the layers that share it; "vLLM Inference Path:
+ * GLM-5.2 as an Example", section "DSA Indexer").
+ *
+ * Exactly n_layers calls of dsa_sparse_mla_fwd with the same batch, indices,
+ * k, scale and shapes, and with layer l's q[l], kv[l], out[l] and lse[l]; the
+ * results are bit-identical to those calls. The layers run as one launch, so
+ * one layer's start-up and tail overlap another's work.
+ *
+ *   n_layers  1 .. 8
+ *   q, out    HOST arrays of n_layers DEVICE pointers, as in dsa_sparse_mla_fwd
+ *   kv        HOST array of n_layers caches: one element type, row width and
+ *             page size (the batch's block table addresses all of them)
+ *   lse       HOST array of n_layers device pointers (entries may be NULL),
+ *             or NULL for no lse in any layer
+ *   workspace device, >= dsa_sparse_mla_layers_workspace_size(n_layers, ...)
+ *
+ * Errors: as dsa_sparse_mla_fwd, plus DSA_ERR_SHAPE for n_layers outside
+ * 1..8 or caches of different page sizes, DSA_ERR_NULL for a NULL q, kv or
+ * out array.
+ */
+size_t dsa_sparse_mla_layers_workspace_size(int32_t n_layers, int32_t total_q, int32_t n_heads,
+                                            int32_t d_latent, int32_t k);
+dsa_status dsa_sparse_mla_fwd_layers(const dsa_batch *batch, int32_t n_layers,
+                                     const void *const *q, int32_t q_dtype, int32_t n_heads,
+                                     int32_t d_latent, int32_t d_rope, const dsa_paged_cache *kv,
+                                     const int32_t *indices, int32_t k, float scale,
+                                     float *const *out, float *const *lse, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
  * Page scores for page-budget selection, the alternative to token top-k that
  * bounds the pages attention reads ("Making GLM-5.2 Sparse on TPUs", section
  * "Make the sparsity unit match the memory unit": a page is ranked by its

@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import ctypes
 from dataclasses import dataclass
-from typing import Optional, Tuple
+from typing import Optional, Sequence, Tuple
 
 import torch
 
@@ -251,6 +251,55 @@ def sparse_mla_fwd(batch: Batch, q: torch.Tensor, kv: PagedCache, indices: torch
                                  0 if lse is None else _dev(lse, "lse", torch.float32), wp, wb,
                                  _stream(q.device)), "dsa_sparse_mla_fwd")
     return out, lse
+
+
+def sparse_mla_layers_workspace_size(n_layers: int, total_q: int, n_heads: int, d_latent: int,
+                                     k: int) -> int:
+    return int(lib.dsa_sparse_mla_layers_workspace_size(n_layers, total_q, n_heads, d_latent, k))
+
+
+def sparse_mla_fwd_layers(batch: Batch, qs: Sequence[torch.Tensor], kvs: Sequence[PagedCache],
+                          indices: torch.Tensor, d_latent: int, scale: float,
+                          outs: Optional[Sequence[torch.Tensor]] = None,
+                          lses: Optional[Sequence[torch.Tensor]] = None,
+                          workspace: Optional[torch.Tensor] = None,
+                          want_lse: bool = True):
+    """IndexShare: sparse_mla_fwd for several layers on one index list, as one call.
+    Returns (outs, lses), lists of per-layer [T, H, d_latent] and [T, H] fp32 tensors."""
+    n = len(qs)
+    if n != len(kvs) or n < 1:
+        raise ValueError("one cache per query tensor, at least one layer")
+    T, H, D = qs[0].shape
+    qd = _DT.get(qs[0].dtype)
+    if qd not in (DSA_F32, DSA_BF16):
+        raise TypeError("q must be float32 or bfloat16")
+    if any(tuple(q.shape) != (T, H, D) or q.dtype != qs[0].dtype for q in qs):
+        raise ValueError("every layer's q must have the same shape and dtype")
+    d_rope = D - d_latent
+    k = indices.shape[1]
+    dev = qs[0].device
+    if outs is None:
+        outs = [torch.empty((T, H, d_latent), dtype=torch.float32, device=dev) for _ in range(n)]
+    if lses is None and want_lse:
+        lses = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in range(n)]
+    need = sparse_mla_layers_workspace_size(n, batch.total_q, H, d_latent, k)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wp = 0 if workspace is None else _dev(workspace, "workspace")
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    q_arr = (ctypes.c_void_p * n)(*[_dev(q, "q") for q in qs])
+    o_arr = (ctypes.c_void_p * n)(*[_dev(o, "out", torch.float32) for o in outs])
+    l_arr = None if lses is None else (ctypes.c_void_p * n)(
+        *[_dev(x, "lse", torch.float32) for x in lses])
+    kv_arr = (DsaPagedCache * n)(*[kv.c() for kv in kvs])
+    b = batch.c()
+    check(lib.dsa_sparse_mla_fwd_layers(
+        ctypes.byref(b), n, ctypes.cast(q_arr, ctypes.c_void_p), qd, H, d_latent, d_rope,
+        kv_arr, _dev(indices, "indices", torch.int32), k, float(scale),
+        ctypes.cast(o_arr, ctypes.c_void_p),
+        None if l_arr is None else ctypes.cast(l_arr, ctypes.c_void_p), wp, wb, _stream(dev)),
+        "dsa_sparse_mla_fwd_layers")
+    return list(outs), (None if lses is None else list(lses))
 
 
 def kv_append(slot_mapping: torch.Tensor, latent: Optional[torch.Tensor] = None,

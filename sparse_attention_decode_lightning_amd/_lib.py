@@ -74,6 +74,11 @@ def _load():
     lib.dsa_sparse_mla_workspace_size.argtypes = [I32, I32, I32, I32]
     lib.dsa_sparse_mla_fwd.restype = ctypes.c_int
     lib.dsa_sparse_mla_fwd.argtypes = [BP, P, I32, I32, I32, I32, CP, P, I32, F, P, P, P, SZ, P]
+    lib.dsa_sparse_mla_layers_workspace_size.restype = SZ
+    lib.dsa_sparse_mla_layers_workspace_size.argtypes = [I32, I32, I32, I32, I32]
+    lib.dsa_sparse_mla_fwd_layers.restype = ctypes.c_int
+    lib.dsa_sparse_mla_fwd_layers.argtypes = [BP, I32, P, I32, I32, I32, I32, CP, P, I32, F, P, P,
+                                              P, SZ, P]
     lib.dsa_indexer_page_scores.restype = ctypes.c_int
     lib.dsa_indexer_page_scores.argtypes = [BP, P, I32, P, I32, I32, CP, I32, P, I64, P]
     lib.dsa_page_scores.restype = ctypes.c_int

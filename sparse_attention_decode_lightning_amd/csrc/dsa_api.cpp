@@ -139,37 +139,82 @@ size_t dsa_sparse_mla_workspace_size(int32_t total_q, int32_t n_heads, int32_t d
   return dsa::mla_workspace_bytes(total_q, n_heads, d_latent, k);
 }
 
+}  // extern "C"
+
+namespace {
+
+// One or more attention layers over one index list: validation common to
+// dsa_sparse_mla_fwd (one layer) and dsa_sparse_mla_fwd_layers.
+dsa_status mla_layers(const dsa_batch *batch, int32_t n_layers, const void *const *q,
+                      int32_t q_dtype, int32_t n_heads, int32_t d_latent, int32_t d_rope,
+                      const dsa_paged_cache *kv, const int32_t *indices, int32_t k, float scale,
+                      float *const *out, float *const *lse, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  BatchArgs bt;
+  dsa_status st = check_batch(batch, &bt);
+  if (st != DSA_OK) return st;
+  if (n_layers < 1 || n_layers > dsa::kMlaMaxLayers) return DSA_ERR_SHAPE;
+  if (kv == nullptr || q == nullptr || out == nullptr) return DSA_ERR_NULL;
+  if (bt.total_q > 0 && indices == nullptr) return DSA_ERR_NULL;
+  if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (n_heads < 1 || d_latent < 1 || d_rope < 0 || k < 1) return DSA_ERR_SHAPE;
+  if (!isfinite(scale)) return DSA_ERR_SHAPE;
+  if (!aligned(indices, 4)) return DSA_ERR_SHAPE;
+  dsa::MlaLayer ly[dsa::kMlaMaxLayers];
+  for (int l = 0; l < n_layers; ++l) {
+    st = check_cache(&kv[l], bt, &ly[l].kv);
+    if (st != DSA_OK) return st;
+    if (bt.total_q > 0 && (q[l] == nullptr || out[l] == nullptr)) return DSA_ERR_NULL;
+    if (ly[l].kv.dtype != q_dtype) return DSA_ERR_DTYPE;
+    if ((int64_t)ly[l].kv.row_elems != (int64_t)d_latent + d_rope) return DSA_ERR_SHAPE;
+    // one block table addresses every layer's cache
+    if (ly[l].kv.page_size != ly[0].kv.page_size) return DSA_ERR_SHAPE;
+    ly[l].q = q[l];
+    ly[l].out = out[l];
+    ly[l].lse = lse == nullptr ? nullptr : lse[l];
+    if (!aligned(ly[l].q, 16) || !aligned(ly[l].out, 16) ||
+        (ly[l].lse != nullptr && !aligned(ly[l].lse, 4)))
+      return DSA_ERR_SHAPE;
+  }
+  const bool mfma_shape = q_dtype == DSA_BF16 && n_heads == 64 && d_latent == 512 && d_rope == 64;
+  if (!mfma_shape && d_latent > 1024) return DSA_ERR_UNSUPPORTED;
+  if (mfma_shape && k > dsa::mla_max_k()) return DSA_ERR_UNSUPPORTED;
+  const size_t need = (size_t)n_layers * dsa::mla_workspace_bytes(bt.total_q, n_heads, d_latent, k);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+    return DSA_ERR_WORKSPACE;
+  if (bt.total_q == 0) return DSA_OK;
+  return launch_status(dsa::launch_sparse_mla(bt, ly, n_layers, q_dtype, n_heads, d_latent,
+                                              d_rope, indices, k, scale, workspace,
+                                              workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
 dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_dtype,
                               int32_t n_heads, int32_t d_latent, int32_t d_rope,
                               const dsa_paged_cache *kv, const int32_t *indices, int32_t k,
                               float scale, float *out, float *lse, void *workspace,
                               size_t workspace_bytes, void *stream) {
-  BatchArgs bt;
-  CacheArgs kc;
-  dsa_status st = check_batch(batch, &bt);
-  if (st != DSA_OK) return st;
-  if (kv == nullptr) return DSA_ERR_NULL;
-  if (bt.total_q > 0 && (q == nullptr || indices == nullptr || out == nullptr)) return DSA_ERR_NULL;
-  st = check_cache(kv, bt, &kc);
-  if (st != DSA_OK) return st;
-  if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
-  if (kc.dtype != q_dtype) return DSA_ERR_DTYPE;
-  if (n_heads < 1 || d_latent < 1 || d_rope < 0 || k < 1) return DSA_ERR_SHAPE;
-  if ((int64_t)kc.row_elems != (int64_t)d_latent + d_rope) return DSA_ERR_SHAPE;
-  if (!isfinite(scale)) return DSA_ERR_SHAPE;
-  if (!aligned(q, 16) || !aligned(indices, 4) || !aligned(out, 16) ||
-      (lse != nullptr && !aligned(lse, 4)))
-    return DSA_ERR_SHAPE;
-  const bool mfma_shape = q_dtype == DSA_BF16 && n_heads == 64 && d_latent == 512 && d_rope == 64;
-  if (!mfma_shape && d_latent > 1024) return DSA_ERR_UNSUPPORTED;
-  if (mfma_shape && k > dsa::mla_max_k()) return DSA_ERR_UNSUPPORTED;
-  const size_t need = dsa::mla_workspace_bytes(bt.total_q, n_heads, d_latent, k);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
-    return DSA_ERR_WORKSPACE;
-  if (bt.total_q == 0) return DSA_OK;
-  return launch_status(dsa::launch_sparse_mla(bt, q, q_dtype, n_heads, d_latent, d_rope, kc,
-                                              indices, k, scale, out, lse, workspace,
-                                              workspace_bytes, static_cast<hipStream_t>(stream)));
+  return mla_layers(batch, 1, &q, q_dtype, n_heads, d_latent, d_rope, kv, indices, k, scale, &out,
+                    &lse, workspace, workspace_bytes, stream);
+}
+
+size_t dsa_sparse_mla_layers_workspace_size(int32_t n_layers, int32_t total_q, int32_t n_heads,
+                                            int32_t d_latent, int32_t k) {
+  if (n_layers < 1 || n_layers > dsa::kMlaMaxLayers) return 0;
+  return (size_t)n_layers * dsa_sparse_mla_workspace_size(total_q, n_heads, d_latent, k);
+}
+
+dsa_status dsa_sparse_mla_fwd_layers(const dsa_batch *batch, int32_t n_layers,
+                                     const void *const *q, int32_t q_dtype, int32_t n_heads,
+                                     int32_t d_latent, int32_t d_rope, const dsa_paged_cache *kv,
+                                     const int32_t *indices, int32_t k, float scale,
+                                     float *const *out, float *const *lse, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  return mla_layers(batch, n_layers, q, q_dtype, n_heads, d_latent, d_rope, kv, indices, k, scale,
+                    out, lse, workspace, workspace_bytes, stream);
 }
 
 dsa_status dsa_indexer_page_scores(const dsa_batch *batch, const void *q_idx, int32_t q_dtype,

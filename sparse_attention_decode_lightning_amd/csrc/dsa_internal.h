@@ -52,13 +52,23 @@ hipError_t launch_topk(const BatchArgs &bt, const float *scores, int64_t ld_scor
                        int32_t unit, int32_t *indices, void *workspace, size_t ws_bytes,
                        hipStream_t stream);
 
+// One attention layer of a sparse MLA call: its query, latent cache and outputs.
+struct MlaLayer {
+  const void *q;
+  CacheArgs kv;
+  float *out;
+  float *lse;  // may be null
+};
+constexpr int kMlaMaxLayers = 8;  // layers one call may take (sharing one index list)
+
 int mla_num_splits(int32_t total_q, int32_t n_heads, int32_t d_latent, int32_t k);
 int mla_max_k();  // largest k of the 64-head bf16 MFMA path
+// workspace of one layer; a call over n layers needs n times this
 size_t mla_workspace_bytes(int32_t total_q, int32_t n_heads, int32_t d_latent, int32_t k);
-hipError_t launch_sparse_mla(const BatchArgs &bt, const void *q, int32_t q_dtype, int32_t n_heads,
-                             int32_t d_latent, int32_t d_rope, const CacheArgs &kv,
-                             const int32_t *indices, int32_t k, float scale, float *out, float *lse,
-                             void *workspace, size_t ws_bytes, hipStream_t stream);
+hipError_t launch_sparse_mla(const BatchArgs &bt, const MlaLayer *layers, int n_layers,
+                             int32_t q_dtype, int32_t n_heads, int32_t d_latent, int32_t d_rope,
+                             const int32_t *indices, int32_t k, float scale, void *workspace,
+                             size_t ws_bytes, hipStream_t stream);
 
 hipError_t launch_page_scores(const BatchArgs &bt, const float *scores, int64_t ld,
                               int32_t page_size, float *page_scores, int64_t ld_pages,

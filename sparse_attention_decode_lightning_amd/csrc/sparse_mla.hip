@@ -180,14 +180,23 @@ __device__ __forceinline__ float group4_sum(float v) {
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+// Per-layer pointers of one launch (kernel argument, indexed by the block's
+// layer). Layers share the batch, the block table and the index list.
+struct MlaLayerArgs {
+  const uint16_t *q[kMlaMaxLayers];
+  const uint8_t *kv[kMlaMaxLayers];
+  int64_t num_pages[kMlaMaxLayers];
+  float *out[kMlaMaxLayers];
+  float *lse[kMlaMaxLayers];
+};
+
 template <bool kOff32>
 __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ cu_q, int batch, int total_q, int max_seq_len, int64_t bt_stride,
-    const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv, int64_t num_pages,
-    int page_size, FastDiv pdiv, const int32_t *__restrict__ indices, int k, int n_splits,
-    int rows_per_split, float scale_log2, float *__restrict__ out, float *__restrict__ lse,
-    float *__restrict__ ws_acc, float *__restrict__ ws_ml) {
+    const MlaLayerArgs layers, int blocks_per_layer, int page_size, FastDiv pdiv,
+    const int32_t *__restrict__ indices, int k, int n_splits, int rows_per_split,
+    float scale_log2, float *__restrict__ ws_acc, float *__restrict__ ws_ml) {
   // ring of row tiles: tile i lives in stage i % kStages
   __shared__ __attribute__((aligned(1024))) uint8_t s_tiles[kStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) uint32_t s_rowid[kMaxRowsPerSplit + kTileN];
@@ -195,12 +204,26 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
   __shared__ float s_ml[kH][2];
   __shared__ int s_over[kMlaWaves];
 
-  // XCD-aware numbering: block id = ((row / 8) * n_splits + split) * 8 + row % 8
-  const int xcd = blockIdx.x % kXcds;
-  const int rest = blockIdx.x / kXcds;
+  // Layers take consecutive ranges of blocks, so one layer's tail overlaps
+  // the next one's start. Within a layer, XCD-aware numbering: block id =
+  // ((row / 8) * n_splits + split) * 8 + row % 8 (blocks_per_layer is a
+  // multiple of 8, so the XCD of a block is its row % 8 in every layer).
+  const int layer = (int)(blockIdx.x / (unsigned)blocks_per_layer);
+  const int bid = (int)blockIdx.x - layer * blocks_per_layer;
+  const int xcd = bid % kXcds;
+  const int rest = bid / kXcds;
   const int split = rest % n_splits;
   const int row = (rest / n_splits) * kXcds + xcd;
   if (row >= total_q) return;
+  const uint16_t *__restrict__ q = layers.q[layer];
+  const uint8_t *__restrict__ kv = layers.kv[layer];
+  const int64_t num_pages = layers.num_pages[layer];
+  float *__restrict__ out = layers.out[layer];
+  float *__restrict__ lse = layers.lse[layer];
+  if (n_splits > 1) {
+    ws_acc += (int64_t)layer * total_q * n_splits * kH * kDL;
+    ws_ml += (int64_t)layer * total_q * n_splits * kH * 2;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, j = lane & 15;
@@ -589,11 +612,18 @@ constexpr int kCombineThreads = 256;
 constexpr int kCombineBlocksPerRow = kH * kDL / 8 / kCombineThreads;  // 16
 
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(
-    int n_splits, const float *__restrict__ ws_acc, const float *__restrict__ ws_ml,
-    float *__restrict__ out, float *__restrict__ lse) {
+    int total_q, int n_splits, const float *__restrict__ ws_acc, const float *__restrict__ ws_ml,
+    const MlaLayerArgs layers) {
   constexpr int kU = 8;
-  const int row = blockIdx.x / kCombineBlocksPerRow;
-  const int i = (blockIdx.x % kCombineBlocksPerRow) * kCombineThreads + threadIdx.x;  // < 4096
+  const int per_layer = total_q * kCombineBlocksPerRow;
+  const int layer = (int)(blockIdx.x / (unsigned)per_layer);
+  const int lb = (int)blockIdx.x - layer * per_layer;
+  const int row = lb / kCombineBlocksPerRow;
+  const int i = (lb % kCombineBlocksPerRow) * kCombineThreads + threadIdx.x;  // < 4096
+  float *__restrict__ out = layers.out[layer];
+  float *__restrict__ lse = layers.lse[layer];
+  ws_acc += (int64_t)layer * total_q * n_splits * kH * kDL;
+  ws_ml += (int64_t)layer * total_q * n_splits * kH * 2;
   const int wv = i >> 10, nt = (i >> 6) & 15, l = i & 63;
   const int head0 = 16 * wv + 4 * (l >> 4), dim = 16 * nt + (l & 15);
   const int64_t split_f4 = kH * kDL / 4;
@@ -737,53 +767,69 @@ size_t mla_workspace_bytes(int32_t total_q, int32_t n_heads, int32_t d_latent, i
   return (size_t)total_q * s * n_heads * (d_latent + 2) * sizeof(float);
 }
 
-hipError_t launch_sparse_mla(const BatchArgs &bt, const void *q, int32_t q_dtype, int32_t n_heads,
-                             int32_t d_latent, int32_t d_rope, const CacheArgs &kv,
-                             const int32_t *indices, int32_t k, float scale, float *out, float *lse,
-                             void *workspace, size_t, hipStream_t stream) {
-  if (bt.total_q == 0) return hipSuccess;
+hipError_t launch_sparse_mla(const BatchArgs &bt, const MlaLayer *ly, int n_layers,
+                             int32_t q_dtype, int32_t n_heads, int32_t d_latent, int32_t d_rope,
+                             const int32_t *indices, int32_t k, float scale, void *workspace,
+                             size_t, hipStream_t stream) {
+  if (bt.total_q == 0 || n_layers < 1) return hipSuccess;
+  if (n_layers > kMlaMaxLayers) return hipErrorInvalidValue;
   const float scale_log2 = scale * kLog2e;
   if (mfma_shape(q_dtype, n_heads, d_latent, d_rope)) {
     const int S = mla_num_splits(bt.total_q, n_heads, d_latent, k);
     const int per = (((k + S - 1) / S) + kTileN - 1) / kTileN * kTileN;
     float *ws_acc = static_cast<float *>(workspace);
-    float *ws_ml = ws_acc == nullptr ? nullptr
-                                     : ws_acc + (size_t)bt.total_q * S * n_heads * d_latent;
+    float *ws_ml = ws_acc == nullptr
+                       ? nullptr
+                       : ws_acc + (size_t)n_layers * bt.total_q * S * n_heads * d_latent;
     const int64_t rows_padded = (int64_t)(bt.total_q + kXcds - 1) / kXcds * kXcds;
-    // 32-bit row offsets (from a base 3072 bytes below the cache) when the
-    // whole pool lies within 4 GiB of that base
-    const uint64_t pool_bytes = (uint64_t)kv.num_pages * (uint64_t)kv.page_size * kRowBytes;
-    auto kern = pool_bytes + 4096 <= (1ull << 32) ? sparse_mla_bf16_kernel<true>
-                                                    : sparse_mla_bf16_kernel<false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(rows_padded * S)), dim3(kMlaThreads), 0, stream,
+    const int64_t bpl = rows_padded * S;
+    if (bpl * n_layers > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    MlaLayerArgs la{};
+    // 32-bit row offsets (from a base 3072 bytes below each cache) when every
+    // layer's pool lies within 4 GiB of that base
+    bool off32 = true;
+    for (int l = 0; l < n_layers; ++l) {
+      la.q[l] = static_cast<const uint16_t *>(ly[l].q);
+      la.kv[l] = static_cast<const uint8_t *>(ly[l].kv.data);
+      la.num_pages[l] = ly[l].kv.num_pages;
+      la.out[l] = ly[l].out;
+      la.lse[l] = ly[l].lse;
+      const uint64_t pool_bytes = (uint64_t)ly[l].kv.num_pages * (uint64_t)ly[l].kv.page_size * kRowBytes;
+      off32 = off32 && pool_bytes + 4096 <= (1ull << 32);
+    }
+    auto kern = off32 ? sparse_mla_bf16_kernel<true> : sparse_mla_bf16_kernel<false>;
+    const int page_size = ly[0].kv.page_size;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(bpl * n_layers)), dim3(kMlaThreads), 0, stream,
                        bt.block_table, bt.seq_lens, bt.cu_q, bt.batch, bt.total_q,
-                       bt.max_seq_len, bt.bt_stride, static_cast<const uint16_t *>(q),
-                       static_cast<const uint8_t *>(kv.data), kv.num_pages, kv.page_size,
-                       make_fast_div((uint32_t)kv.page_size), indices, k, S, per, scale_log2, out,
-                       lse, ws_acc, ws_ml);
+                       bt.max_seq_len, bt.bt_stride, la, (int)bpl, page_size,
+                       make_fast_div((uint32_t)page_size), indices, k, S, per, scale_log2,
+                       ws_acc, ws_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
-    hipLaunchKernelGGL(mla_combine_kernel, dim3(bt.total_q * kCombineBlocksPerRow),
-                       dim3(kCombineThreads), 0, stream,
-                       S, ws_acc, ws_ml, out, lse);
+    hipLaunchKernelGGL(mla_combine_kernel,
+                       dim3((unsigned)((int64_t)bt.total_q * kCombineBlocksPerRow * n_layers)),
+                       dim3(kCombineThreads), 0, stream, bt.total_q, S, ws_acc, ws_ml, la);
     return hipGetLastError();
   }
-  if (q_dtype == DSA_F32) {
-    hipLaunchKernelGGL(sparse_mla_generic_kernel<float>, dim3(bt.total_q * n_heads), dim3(256), 0,
-                       stream, bt.block_table, bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len,
-                       bt.bt_stride,
-                       static_cast<const float *>(q), static_cast<const float *>(kv.data),
-                       kv.num_pages, kv.page_size, n_heads, d_latent, d_rope, indices, k,
-                       scale_log2, out, lse);
-  } else {
-    hipLaunchKernelGGL(sparse_mla_generic_kernel<uint16_t>, dim3(bt.total_q * n_heads), dim3(256),
-                       0, stream, bt.block_table, bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len,
-                       bt.bt_stride,
-                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv.data),
-                       kv.num_pages, kv.page_size, n_heads, d_latent, d_rope, indices, k,
-                       scale_log2, out, lse);
+  for (int l = 0; l < n_layers; ++l) {
+    const CacheArgs &kv = ly[l].kv;
+    if (q_dtype == DSA_F32) {
+      hipLaunchKernelGGL(sparse_mla_generic_kernel<float>, dim3(bt.total_q * n_heads), dim3(256), 0,
+                         stream, bt.block_table, bt.seq_lens, bt.cu_q, bt.batch, bt.total_q,
+                         bt.max_seq_len, bt.bt_stride, static_cast<const float *>(ly[l].q),
+                         static_cast<const float *>(kv.data), kv.num_pages, kv.page_size, n_heads,
+                         d_latent, d_rope, indices, k, scale_log2, ly[l].out, ly[l].lse);
+    } else {
+      hipLaunchKernelGGL(sparse_mla_generic_kernel<uint16_t>, dim3(bt.total_q * n_heads), dim3(256),
+                         0, stream, bt.block_table, bt.seq_lens, bt.cu_q, bt.batch, bt.total_q,
+                         bt.max_seq_len, bt.bt_stride, static_cast<const uint16_t *>(ly[l].q),
+                         static_cast<const uint16_t *>(kv.data), kv.num_pages, kv.page_size,
+                         n_heads, d_latent, d_rope, indices, k, scale_log2, ly[l].out, ly[l].lse);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace dsa

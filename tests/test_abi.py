@@ -193,3 +193,38 @@ def test_empty_batch_is_a_validated_no_op():
     assert L.lib.dsa_page_topk(ctypes.byref(b), None, 1, 64, 0, None, None, None, 0, None) == 2
     # with queries, the same NULL arrays are errors
     assert _idx(q=None) == 1 and _topk(idx=None) == 1 and _mla(out=None) == 1
+
+
+def _mla_layers(n=3, b=None, q=True, qd=L.DSA_BF16, caches=None, idx=FAKE, out=True, lse=True,
+                ws=FAKE, wsb=1 << 40):
+    b = _batch() if b is None else b
+    caches = [_cache(row_elems=576) for _ in range(max(n, 1))] if caches is None else caches
+    kv = (L.DsaPagedCache * len(caches))(*caches) if caches is not False else None
+    arr = lambda: (ctypes.c_void_p * max(n, 1))(*([FAKE] * max(n, 1)))
+    qa, oa, la = (arr() if q else None), (arr() if out else None), (arr() if lse else None)
+    c = lambda a: None if a is None else ctypes.cast(a, ctypes.c_void_p)
+    return L.lib.dsa_sparse_mla_fwd_layers(ctypes.byref(b), n, c(qa), qd, 64, 512, 64,
+                                           kv, idx, 2048, 0.0625, c(oa), c(la), ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), 2), (dict(n=9), 2),
+    (dict(q=False), 1), (dict(out=False), 1), (dict(caches=False), 1), (dict(idx=None), 1),
+    (dict(caches=[_cache(row_elems=576), _cache(row_elems=576, page_size=32),
+                  _cache(row_elems=576)]), 2),                    # one block table, one page size
+    (dict(caches=[_cache(row_elems=576), _cache(row_elems=512), _cache(row_elems=576)]), 2),
+    (dict(caches=[_cache(row_elems=576), _cache(row_elems=576, dtype=L.DSA_F32),
+                  _cache(row_elems=576)]), 3),
+    (dict(ws=None), 4),
+])
+def test_mla_layers_rejects_bad_arguments(kw, code):
+    assert _mla_layers(**kw) == code
+
+
+def test_mla_layers_workspace_and_empty_batch():
+    one = L.lib.dsa_sparse_mla_workspace_size(32, 64, 512, 2048)
+    assert L.lib.dsa_sparse_mla_layers_workspace_size(3, 32, 64, 512, 2048) == 3 * one
+    assert L.lib.dsa_sparse_mla_layers_workspace_size(0, 32, 64, 512, 2048) == 0
+    b = L.DsaBatch(block_table=None, seq_lens=None, cu_q=None, batch=0, bt_stride=0, total_q=0,
+                   max_seq_len=0, max_q=0)
+    assert _mla_layers(b=b, idx=None, lse=False, ws=None, wsb=0) == 0

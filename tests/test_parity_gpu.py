@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import sparse_attention_decode_lightning_amd as dsa
 from tests import parity as P
 from workloads import WORKLOADS, host_view, make_inputs, small_variant, to_device
 
@@ -86,6 +87,34 @@ def test_indexshare_layers_reuse_one_topk(dev):
     for l, (out, lse) in enumerate(outs):
         P.check_mla(inp, l, idx, out, lse, rows, host)
     assert not torch.equal(outs[0][0], outs[1][0])
+
+
+@pytest.mark.parametrize("name,n_layers", [("indexshare_b64", 3), ("tiny", 2)])
+def test_mla_layers_call_equals_one_call_per_layer(name, n_layers, dev):
+    """IndexShare as one call over several layers is bit-identical to one call per
+    layer (MFMA path with splits; generic path), canaries past every output intact,
+    and lse may be left out."""
+    wl = small_variant(name, batch=3, lens=(3000, 2100, 5000) if name != "tiny" else (256, 90, 17),
+                       topk=1024 if name != "tiny" else 64, n_layers=n_layers)
+    print(f"[mla-layers] {name} x{n_layers}", flush=True)
+    inp = to_device(make_inputs(wl), dev)
+    _, idx, ref = P.run_gpu(inp)
+    T = inp.total_q
+    kvs = [dsa.PagedCache(inp.kv_cache[l]) for l in range(n_layers)]
+    outs = [torch.full((T + 1, wl.mla_heads, wl.d_latent), float("nan"), device=dev)
+            for _ in range(n_layers)]
+    lses = [torch.full((T + 1, wl.mla_heads), float("nan"), device=dev) for _ in range(n_layers)]
+    dsa.sparse_mla_fwd_layers(P.batch_of(inp), [inp.q_mla[l] for l in range(n_layers)], kvs, idx,
+                              wl.d_latent, wl.scale, outs=[o[:T] for o in outs],
+                              lses=[x[:T] for x in lses])
+    o2, l2 = dsa.sparse_mla_fwd_layers(P.batch_of(inp), [inp.q_mla[l] for l in range(n_layers)],
+                                       kvs, idx, wl.d_latent, wl.scale, want_lse=False)
+    torch.cuda.synchronize()
+    assert l2 is None
+    for l in range(n_layers):
+        assert torch.equal(outs[l][:T], ref[l][0]) and torch.equal(lses[l][:T], ref[l][1]), l
+        assert torch.equal(o2[l], ref[l][0]), l
+        assert torch.isnan(outs[l][T]).all() and torch.isnan(lses[l][T]).all()
 
 
 def test_mla_restart_on_late_large_logits(dev):
