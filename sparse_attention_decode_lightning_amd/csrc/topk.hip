@@ -360,7 +360,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void to
 }
 
 // Rows longer than one register block (32K): two phases on the same selection.
-// Phase 1 selects the top-k of every 16K-position chunk of a row (one
+// Phase 1 selects the top-k of every chunk of a row (16K positions; 32K
+// past 128K, where fewer survivors make the merge cheaper) (one
 // 1024-thread workgroup per row and chunk) and writes the chunk's survivors,
 // keys and positions, in ascending position order to slots [c k, c k + m_c)
 // of the row's workspace, m_c = min(k, candidates of the chunk). Phase 2 (one
@@ -369,21 +370,28 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void to
 // exact: a position in the row's top-k is also in its chunk's top-k under the
 // same order, and slot order is position order among the survivors, so ties
 // still go to the lower position.
-constexpr int kSplitChunk = 16 * kRegThreads;    // phase-1 chunk: 1024 threads x 16 keys
 constexpr int kSplitCands = 32 * kRegThreads;    // phase-2 slots: 1024 threads x 32 keys
 
-int split_chunks(int32_t max_seq_len) { return (max_seq_len + kSplitChunk - 1) / kSplitChunk; }
+// phase-1 chunk: 1024 threads x 16 (or 32) keys
+int split_chunk(int32_t max_seq_len) {
+  return max_seq_len > 128 * kRegThreads ? 32 * kRegThreads : 16 * kRegThreads;
+}
+int split_chunks(int32_t max_seq_len) {
+  const int c = split_chunk(max_seq_len);
+  return (max_seq_len + c - 1) / c;
+}
 
 bool split_path(int32_t max_seq_len, int32_t k) {
   return max_seq_len > 32 * kRegThreads && (int64_t)split_chunks(max_seq_len) * k <= kSplitCands;
 }
 
+template <int R>
 __global__ __launch_bounds__(kRegThreads) __attribute__((amdgpu_waves_per_eu(8))) void topk_chunk_kernel(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
     int total_q, int max_seq_len, int n_max, FastDiv unit, const float *__restrict__ scores,
     int64_t ld, int k, int nc,
     uint32_t *__restrict__ ws_key, int32_t *__restrict__ ws_pos) {
-  constexpr int R = kSplitChunk / kRegThreads;
+  constexpr int kSplitChunk = R * kRegThreads;
   __shared__ SelectShared<kRegThreads / kWave, R, 4, 2> sh;
   const int c = blockIdx.x, row = blockIdx.y;
   const int tid = threadIdx.x;
@@ -423,7 +431,7 @@ __global__ __launch_bounds__(kRegThreads) __attribute__((amdgpu_waves_per_eu(8))
 template <int R>
 __global__ __launch_bounds__(kRegThreads) void topk_split_merge_kernel(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
-    int total_q, int max_seq_len, int n_max, FastDiv unit, int k, FastDiv kdiv, int nc,
+    int total_q, int max_seq_len, int n_max, FastDiv unit, int k, FastDiv kdiv, int nc, int chunk,
     const uint32_t *__restrict__ ws_key,
     const int32_t *__restrict__ ws_pos, int32_t *__restrict__ indices) {
   __shared__ SelectShared<kRegThreads / kWave, R, 4, 2> sh;
@@ -445,7 +453,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_split_merge_kernel(
     const int j = sel_cand<R>(u);
     const int c = (int)fast_div((uint32_t)j, kdiv);
     const int s = j - c * k;
-    const int m = min(min(max(n - c * kSplitChunk, 0), kSplitChunk), k);  // survivors of chunk c
+    const int m = min(min(max(n - c * chunk, 0), chunk), k);  // survivors of chunk c
     const bool ok = j < nc * k && s < m;
     key[u] = ok ? ikey[j] : 0u;
     pos[u] = ok ? ipos[j] : -1;
@@ -503,7 +511,9 @@ hipError_t launch_topk(const BatchArgs &bt, const float *scores, int64_t ld, int
     if (bt.total_q > 65535) return hipErrorInvalidConfiguration;
     uint32_t *ws_key = static_cast<uint32_t *>(workspace);
     int32_t *ws_pos = reinterpret_cast<int32_t *>(ws_key + (size_t)bt.total_q * nc * k);
-    hipLaunchKernelGGL(topk_chunk_kernel, dim3(nc, bt.total_q), dim3(kRegThreads), 0, stream,
+    const int chunk = split_chunk(n_max);
+    auto ck = chunk == 32 * kRegThreads ? topk_chunk_kernel<32> : topk_chunk_kernel<16>;
+    hipLaunchKernelGGL(ck, dim3(nc, bt.total_q), dim3(kRegThreads), 0, stream,
                        bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, n_max, fu,
                        scores, ld, k, nc, ws_key, ws_pos);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -513,7 +523,7 @@ hipError_t launch_topk(const BatchArgs &bt, const float *scores, int64_t ld, int
                                              : topk_split_merge_kernel<32>;
     hipLaunchKernelGGL(merge, dim3(bt.total_q), dim3(kRegThreads), 0, stream, bt.seq_lens,
                        bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, n_max, fu, k,
-                       make_fast_div((uint32_t)k), nc, ws_key, ws_pos, indices);
+                       make_fast_div((uint32_t)k), nc, chunk, ws_key, ws_pos, indices);
     return hipGetLastError();
   }
   const size_t lds = (size_t)kChunk * sizeof(uint32_t);

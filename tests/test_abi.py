@@ -134,8 +134,10 @@ def test_mla_rejects_bad_arguments(kw, code):
 
 def test_workspace_sizes_are_pure_functions_of_bounds():
     assert L.lib.dsa_topk_workspace_size(32, 8192, 2048) == 0
-    # rows over 16K: keys and positions of k survivors per 16K-position chunk
-    assert L.lib.dsa_topk_workspace_size(32, 245760, 2048) == 32 * 15 * 2048 * 8
+    # rows over 32K: keys and positions of k survivors per chunk (16K positions,
+    # 32K past 128K)
+    assert L.lib.dsa_topk_workspace_size(32, 245760, 2048) == 32 * 8 * 2048 * 8
+    assert L.lib.dsa_topk_workspace_size(64, 131072, 2048) == 64 * 8 * 2048 * 8
     s = L.lib.dsa_sparse_mla_workspace_size(32, 64, 512, 2048)
     assert s > 0 and s == L.lib.dsa_sparse_mla_workspace_size(32, 64, 512, 2048)
     assert L.lib.dsa_sparse_mla_workspace_size(4096, 64, 512, 2048) == 0

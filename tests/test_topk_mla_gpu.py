@@ -2,8 +2,8 @@
 
 * Top-k on synthetic score rows with ties (quantized, all equal, +0.0 / -0.0
   mixes) and continuous scores, at row lengths that reach every dispatch path
-  (one register block of 8, 16 or 32 keys per thread; 16K chunks then a
-  merge; the LDS chunks past 256K). The oracle's stable sort fixes the unique
+  (one register block of 8, 16 or 32 keys per thread; 16K or 32K chunks then
+  a merge; the LDS chunks for large k). The oracle's stable sort fixes the unique
   answer (ties toward the lower position), so the comparison is exact.
 * Sparse MLA on caller-made index lists: repeated positions (counted twice),
   -1 padding, positions past the row's causal bound and past the sequence
@@ -49,12 +49,15 @@ def _score_rows(kind: str, lens, seed: int) -> list:
 
 TOPK_CASES = [
     # (row lengths, k): one register pass with 8, 16 and 32 keys per thread,
-    # 16K chunks then a merge, and 32K LDS chunks past 256K positions
+    # 16K chunks then a merge (rows to 128K), 32K chunks then a merge (to
+    # 512K at k = 2048), and 32K LDS chunks where the merge would take more
+    # than 32K survivors (large k)
     ((300, 8192, 5), 2048),
     ((12000, 16384), 2048),
     ((20000, 32768), 2048),
     ((70000, 33000, 1000), 2048),
-    ((300000,), 2048),
+    ((300000, 140000), 2048),
+    ((100000, 50000), 8192),
     ((5000, 64), 64),
 ]
 
