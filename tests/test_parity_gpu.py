@@ -243,3 +243,44 @@ def test_graph_replay_matches_eager(dev):
         for o, r in zip(outs, ref_out):
             assert torch.equal(o, r), f"replay {i}: outputs differ"
         del junk
+
+
+def _random_cases(n: int, seed: int):
+    """Seeded random shapes across the dispatch space: page sizes that do and do not
+    hold whole 64-key blocks, 16/32/64 indexer heads, bf16 and fp8 keys, query counts
+    0..5 per sequence (some groups short of four), lengths from 1 to past 32K (the
+    two-phase top-k), k from 64 to 2048."""
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(g.integers(1, 5))
+        lens = tuple(int(x) for x in g.choice([1, 7, 64, 65, 300, 2049, 5000, 17000, 40000], size=B))
+        qs = tuple(int(min(L, x)) for L, x in zip(lens, g.integers(0, 6, size=B)))
+        if sum(qs) == 0:
+            qs = (1,) + qs[1:]
+        base = "indexshare_b64" if g.random() < 0.5 else "decode_b32_l8k"
+        out.append((f"rand{i}", small_variant(
+            base, seed=100 + i, batch=B, lens=lens, q_per_seq=qs,
+            page_size=int(g.choice([16, 48, 64, 128])), idx_heads=int(g.choice([16, 32, 64])),
+            topk=int(g.choice([64, 512, 2048])), n_layers=1)))
+    return out
+
+
+@pytest.mark.parametrize("name,wl", _random_cases(12, seed=7), ids=[c[0] for c in _random_cases(12, 7)])
+def test_random_shapes_parity(name, wl, dev):
+    """Scores within 1e-2 RMS, top-k identical on the GPU's scores and within the band
+    end to end, index invariants, and MLA on a sample of rows, for random shapes."""
+    print(f"[parity-rand] {name} lens={wl.lens} q={wl.q_per_seq} P={wl.page_size} "
+          f"H={wl.idx_heads} k={wl.topk} keys={wl.idx_k_dtype}", flush=True)
+    inp_h = make_inputs(wl)
+    inp = to_device(inp_h, dev)
+    host = host_view(inp_h)
+    scores, idx, outs = P.run_gpu(inp)
+    rows = sorted(set(np.random.default_rng(1).choice(inp.total_q, size=min(6, inp.total_q),
+                                                      replace=False).tolist()))
+    ref_scores = P.check_scores(inp, scores, rows, host)
+    P.check_topk_identical(scores, idx, rows, inp, wl.topk)
+    P.check_topk_band(ref_scores, idx, rows, wl.topk)
+    P.check_invariants(inp, idx, wl.topk)
+    out, lse = outs[0]
+    P.check_mla(inp, 0, idx, out, lse, rows, host)
