@@ -48,9 +48,11 @@ hipError_t launch_indexer_page_scores(const BatchArgs &bt, const void *q_idx, co
 
 size_t topk_workspace_bytes(int32_t total_q, int32_t max_cands, int32_t k);
 bool topk_supported(int32_t max_cands, int32_t k);
+// expand (page candidates only): also write the kept pages' positions there
+// when the selection kernel can; *expanded tells whether it did.
 hipError_t launch_topk(const BatchArgs &bt, const float *scores, int64_t ld_scores, int32_t k,
                        int32_t unit, int32_t *indices, void *workspace, size_t ws_bytes,
-                       hipStream_t stream);
+                       hipStream_t stream, int32_t *expand = nullptr, bool *expanded = nullptr);
 
 // One attention layer of a sparse MLA call: its query, latent cache and outputs.
 struct MlaLayer {

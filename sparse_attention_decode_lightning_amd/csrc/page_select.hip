@@ -73,9 +73,12 @@ hipError_t launch_page_topk(const BatchArgs &bt, const float *page_scores, int64
                             int32_t page_size, int32_t kp, int32_t *pages, int32_t *indices,
                             void *workspace, size_t ws_bytes, hipStream_t stream) {
   if (bt.total_q == 0) return hipSuccess;
+  // the one-workgroup selection expands its pages itself; the longer paths
+  // leave it to expand_pages_kernel
+  bool expanded = false;
   hipError_t e = launch_topk(bt, page_scores, ld_pages, kp, page_size, pages, workspace, ws_bytes,
-                             stream);
-  if (e != hipSuccess || indices == nullptr) return e;
+                             stream, indices, &expanded);
+  if (e != hipSuccess || indices == nullptr || expanded) return e;
   if (bt.total_q > 65535) return hipErrorInvalidConfiguration;
   const int64_t k = (int64_t)kp * page_size;
   const dim3 grid((unsigned)((k + kPageThreads - 1) / kPageThreads), (unsigned)bt.total_q);

@@ -329,12 +329,16 @@ constexpr int kRegThreads = 1024;
 // bin is kept whole, a ballot-based ordered emit). The row's scores are
 // requested before its length is known (every load stays below
 // max_seq_len <= ld) and masked afterwards.
+// With `expand` set (a page budget: candidates are pages of `unit`
+// positions), the workgroup then also writes the token positions its kept
+// pages hold: expand[row][i * unit + o] = page_i * unit + o when that is <= t,
+// else -1.
 template <int NT, int R>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void topk_reg_kernel(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q, int batch,
     int total_q, int max_seq_len, int n_max, FastDiv unit, const float *__restrict__ scores,
-    int64_t ld, int k,
-    int32_t *__restrict__ indices) {
+    int64_t ld, int k, int32_t *__restrict__ indices, int32_t *__restrict__ expand,
+    int unit_size) {
   constexpr int kRegThreads = NT;
   __shared__ SelectShared<NT / kWave, R> sh;
   const int row = blockIdx.x;
@@ -351,12 +355,23 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void to
   int32_t *out = indices + (int64_t)row * k;
   if (n <= k) {
     for (int i = tid; i < k; i += kRegThreads) out[i] = i < n ? i : -1;
-    return;
-  }
-  uint32_t key[R];
+  } else {
+    uint32_t key[R];
 #pragma unroll
-  for (int u = 0; u < R; ++u) key[u] = order_key(v[u]);
-  select_run(key, n, k, sh, [&](int u, int slot) { out[slot] = sel_cand<R>(u); });
+    for (int u = 0; u < R; ++u) key[u] = order_key(v[u]);
+    select_run(key, n, k, sh, [&](int u, int slot) { out[slot] = sel_cand<R>(u); });
+  }
+  if (expand == nullptr) return;
+  __syncthreads();  // the row's kept pages, written above by the workgroup, are visible
+  const int t = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, row).t;
+  const int P = unit_size;
+  int32_t *dst = expand + (int64_t)row * k * P;
+  for (int j = tid; j < k * P; j += kRegThreads) {
+    const int i = (int)fast_div((uint32_t)j, unit);
+    const int pg = out[i];
+    const int pos = pg * P + (j - i * P);
+    dst[j] = (pg >= 0 && pos <= t) ? pos : -1;
+  }
 }
 
 // Rows longer than one register block (32K): two phases on the same selection.
@@ -491,18 +506,26 @@ bool topk_supported(int32_t max_seq_len, int32_t k) {
 
 hipError_t launch_topk(const BatchArgs &bt, const float *scores, int64_t ld, int32_t k,
                        int32_t unit, int32_t *indices, void *workspace, size_t,
-                       hipStream_t stream) {
+                       hipStream_t stream, int32_t *expand, bool *expanded) {
+  if (expanded != nullptr) *expanded = false;
   if (bt.total_q == 0) return hipSuccess;
   // candidates of a row: positions (unit 1) or groups of `unit` positions
   const int n_max = candidate_bound(bt.max_seq_len, unit);
   const FastDiv fu = make_fast_div((uint32_t)unit);
   if (n_max <= 32 * kRegThreads) {
-    auto kernel = n_max <= 8 * kRegThreads    ? topk_reg_kernel<kRegThreads, 8>
-                  : n_max <= 16 * kRegThreads ? topk_reg_kernel<kRegThreads, 16>
-                                              : topk_reg_kernel<kRegThreads, 32>;
-    hipLaunchKernelGGL(kernel, dim3(bt.total_q), dim3(kRegThreads), 0, stream, bt.seq_lens,
+    // short rows (a page budget's candidates, small k) on 256 threads: a
+    // smaller workgroup reaches the same selection with less barrier latency
+    auto kernel = n_max <= 256                 ? topk_reg_kernel<256, 1>
+                  : n_max <= 1024              ? topk_reg_kernel<256, 4>
+                  : n_max <= 4 * kRegThreads   ? topk_reg_kernel<kRegThreads, 4>
+                  : n_max <= 8 * kRegThreads   ? topk_reg_kernel<kRegThreads, 8>
+                  : n_max <= 16 * kRegThreads  ? topk_reg_kernel<kRegThreads, 16>
+                                               : topk_reg_kernel<kRegThreads, 32>;
+    const int nt = n_max <= 1024 ? 256 : kRegThreads;
+    hipLaunchKernelGGL(kernel, dim3(bt.total_q), dim3(nt), 0, stream, bt.seq_lens,
                        bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, n_max, fu, scores, ld, k,
-                       indices);
+                       indices, expand, unit);
+    if (expanded != nullptr) *expanded = expand != nullptr;
     return hipGetLastError();
   }
   hipError_t e;
