@@ -79,7 +79,7 @@ typedef enum {
   DSA_ERR_SHAPE = 2,       /* a size, stride or bound is out of range or inconsistent */
   DSA_ERR_DTYPE = 3,       /* an element type is not allowed for this argument */
   DSA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the size query returns */
-  DSA_ERR_UNSUPPORTED = 5, /* a valid combination this build has no kernel for */
+  DSA_ERR_UNSUPPORTED = 5, /* a valid combination the library has no kernel for */
   DSA_ERR_LAUNCH = 6       /* the HIP runtime rejected a kernel launch */
 } dsa_status;
 
