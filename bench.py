@@ -174,6 +174,23 @@ STAGE_KERNELS = {
 COPY_PROBE_BYTES = 256 << 20
 
 
+def read_stream_gbs(nbytes: int, flush, stream, reps: int = 5) -> float:
+    """Median rate of a plain device read (a sum over an int64 buffer) of nbytes,
+    each run after reading the 1 GiB eviction buffer, timed with HIP events."""
+    buf = torch.ones(max(1, nbytes // 8), dtype=torch.int64, device=flush.device)
+    ms = []
+    for _ in range(reps):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        buf.sum()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    del buf
+    return nbytes / (float(np.median(ms)) * 1e-3) / 1e9
+
+
 def committed_traffic(workload: str, stage: str):
     """HBM bytes per call of a stage, from rocprofv3 FETCH_SIZE/WRITE_SIZE counters taken on
     the current kernel sources and scaled by a plain copy of known size; None otherwise."""
@@ -492,6 +509,12 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": hbm_gbs / HBM_PEAK_GBS}
+        # the same bytes as one plain read stream on this machine, after the same
+        # eviction: the rate a perfect streaming kernel of this size could reach
+        rs = read_stream_gbs(int(d_bytes), flush, stream)
+        roof.update(ref_read_gbs=rs, frac_of_ref_read=hbm_gbs / rs,
+                    ref_read="torch int64 sum over the same byte count after the same eviction "
+                             "(a practical streaming-read rate at this size, not a peak)")
     line = {
         "metric": "sparse-decode query tokens/s at B=32,L=8K,topk=2048; achieved HBM GB/s",
         "value": T / (ms * 1e-3),
