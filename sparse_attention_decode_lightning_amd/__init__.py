@@ -265,10 +265,13 @@ def sparse_mla_fwd_layers(batch: Batch, qs: Sequence[torch.Tensor], kvs: Sequenc
                           workspace: Optional[torch.Tensor] = None,
                           want_lse: bool = True):
     """IndexShare: sparse_mla_fwd for several layers on one index list, as one call.
-    Returns (outs, lses), lists of per-layer [T, H, d_latent] and [T, H] fp32 tensors."""
+    Returns (outs, lses), lists of per-layer [T, H, d_latent] and [T, H] fp32 tensors;
+    an entry of `lses` may be None (no lse for that layer)."""
     n = len(qs)
     if n != len(kvs) or n < 1:
         raise ValueError("one cache per query tensor, at least one layer")
+    if (outs is not None and len(outs) != n) or (lses is not None and len(lses) != n):
+        raise ValueError("outs and lses need one entry per layer")
     T, H, D = qs[0].shape
     qd = _DT.get(qs[0].dtype)
     if qd not in (DSA_F32, DSA_BF16):
@@ -290,7 +293,7 @@ def sparse_mla_fwd_layers(batch: Batch, qs: Sequence[torch.Tensor], kvs: Sequenc
     q_arr = (ctypes.c_void_p * n)(*[_dev(q, "q") for q in qs])
     o_arr = (ctypes.c_void_p * n)(*[_dev(o, "out", torch.float32) for o in outs])
     l_arr = None if lses is None else (ctypes.c_void_p * n)(
-        *[_dev(x, "lse", torch.float32) for x in lses])
+        *[None if x is None else _dev(x, "lse", torch.float32) for x in lses])
     kv_arr = (DsaPagedCache * n)(*[kv.c() for kv in kvs])
     b = batch.c()
     check(lib.dsa_sparse_mla_fwd_layers(

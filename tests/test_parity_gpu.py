@@ -109,11 +109,16 @@ def test_mla_layers_call_equals_one_call_per_layer(name, n_layers, dev):
                               lses=[x[:T] for x in lses])
     o2, l2 = dsa.sparse_mla_fwd_layers(P.batch_of(inp), [inp.q_mla[l] for l in range(n_layers)],
                                        kvs, idx, wl.d_latent, wl.scale, want_lse=False)
+    # lse for some layers only (a NULL entry in the lse array)
+    some = [x[:T].clone().fill_(float("nan")) if l % 2 == 0 else None for l, x in enumerate(lses)]
+    o3, l3 = dsa.sparse_mla_fwd_layers(P.batch_of(inp), [inp.q_mla[l] for l in range(n_layers)],
+                                       kvs, idx, wl.d_latent, wl.scale, lses=some)
     torch.cuda.synchronize()
     assert l2 is None
     for l in range(n_layers):
         assert torch.equal(outs[l][:T], ref[l][0]) and torch.equal(lses[l][:T], ref[l][1]), l
-        assert torch.equal(o2[l], ref[l][0]), l
+        assert torch.equal(o2[l], ref[l][0]) and torch.equal(o3[l], ref[l][0]), l
+        assert (l3[l] is None) if l % 2 else torch.equal(l3[l], ref[l][1]), l
         assert torch.isnan(outs[l][T]).all() and torch.isnan(lses[l][T]).all()
 
 
