@@ -106,7 +106,11 @@ typedef struct {
  * rows contiguous. For DSA_FP8_E4M3 `scale` holds one fp32 dequantisation
  * factor per token, [num_pages, page_size], and the stored key is
  * scale * e4m3(byte) ("GLM-5.2 on vLLM Ascend ...", section "7. GLM-5.2
- * shared-indexer construction": FP8 e4m3 keys carry FP32 scales). */
+ * shared-indexer construction": FP8 e4m3 keys carry FP32 scales). Scales
+ * are finite and >= 0, as dsa_kv_append writes them (max|k| / 448); the
+ * streaming indexer applies a key's scale after the ReLU, which equals the
+ * definition only for non-negative scales, so a negative scale gives
+ * unspecified scores. */
 typedef struct {
   const void *data;   /* device */
   const float *scale; /* device [num_pages, page_size]; required for fp8, else ignored */
@@ -203,9 +207,11 @@ size_t dsa_sparse_mla_workspace_size(int32_t total_q, int32_t n_heads, int32_t d
  *   lse      device [total_q, n_heads] fp32 output, or NULL
  *   workspace device, >= dsa_sparse_mla_workspace_size(total_q, n_heads, d_latent, k)
  *
+ *   scale    finite and > 0
+ *
  * Errors: DSA_ERR_NULL (a NULL kv, or with total_q > 0 a NULL q, out or
  * `indices`: a layer that has neither its own nor a shared top-k buffer is
- * rejected), DSA_ERR_SHAPE, DSA_ERR_DTYPE,
+ * rejected), DSA_ERR_SHAPE (also a scale that is not finite and positive), DSA_ERR_DTYPE,
  * DSA_ERR_WORKSPACE, DSA_ERR_LAUNCH.
  */
 dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_dtype,

@@ -3,8 +3,10 @@
 Thin torch-facing binding of the C-ABI library ``libdsa.so`` (see
 ``include/dsa.h``). PyTorch only supplies device memory and the current
 stream; every step runs in the library's HIP kernels. Each wrapper checks
-dtypes, shapes, devices and contiguity, passes raw pointers, and raises
-:class:`DSAError` on a non-zero status.
+dtypes, shapes, devices and contiguity (the batch's arrays against its
+sequence count, and every per-row tensor, caller-supplied outputs included,
+against the batch's ``total_q``, since the kernels size their work from it),
+passes raw pointers, and raises :class:`DSAError` on a non-zero status.
 """
 
 from __future__ import annotations
@@ -57,6 +59,17 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _rows(t: torch.Tensor, name: str, batch: "Batch", shape_tail=None) -> None:
+    """The kernels size their work from batch.total_q: a per-row tensor must hold at
+    least that many rows (and, when given, exactly the trailing shape)."""
+    if t.dim() < 1 or t.shape[0] < batch.total_q:
+        raise ValueError(f"{name} has {t.shape[0] if t.dim() else 0} rows, the batch has "
+                         f"total_q = {batch.total_q}")
+    if shape_tail is not None and tuple(t.shape[1:]) != tuple(shape_tail):
+        raise ValueError(f"{name} must be [rows, {', '.join(map(str, shape_tail))}], got "
+                         f"{tuple(t.shape)}")
+
+
 @dataclass
 class Batch:
     """Packed batch metadata: device arrays plus their host-side bounds."""
@@ -69,6 +82,14 @@ class Batch:
     max_q: int
 
     def c(self) -> DsaBatch:
+        B = int(self.seq_lens.shape[0]) if self.seq_lens.dim() == 1 else -1
+        if B < 0:
+            raise ValueError("seq_lens must be [B]")
+        if self.cu_q.dim() != 1 or self.cu_q.shape[0] != B + 1:
+            raise ValueError(f"cu_q must be [B + 1] = [{B + 1}], got {tuple(self.cu_q.shape)}")
+        if self.block_table.dim() != 2 or self.block_table.shape[0] != B:
+            raise ValueError(f"block_table must be [B = {B}, bt_stride], got "
+                             f"{tuple(self.block_table.shape)}")
         return DsaBatch(
             _dev(self.block_table, "block_table", torch.int32),
             _dev(self.seq_lens, "seq_lens", torch.int32),
@@ -110,11 +131,14 @@ def indexer_scores(batch: Batch, q_idx: torch.Tensor, w: torch.Tensor, keys: Pag
         raise TypeError("q_idx must be float32 or bfloat16")
     if tuple(w.shape) != (T, H):
         raise ValueError("w must be [T, n_heads]")
+    _rows(q_idx, "q_idx", batch)
     if scores is None:
         scores = torch.empty((T, max(1, batch.max_seq_len)), dtype=torch.float32,
                              device=q_idx.device)
     if scores.dim() != 2 or scores.shape[0] != T:
         raise ValueError("scores must be [T, ld]")
+    if scores.shape[1] < batch.max_seq_len:
+        raise ValueError("scores rows must hold max_seq_len entries")
     b, kc = batch.c(), keys.c()
     check(lib.dsa_indexer_scores(ctypes.byref(b), _dev(q_idx, "q_idx"), qd,
                                  _dev(w, "w", torch.float32), H, D, ctypes.byref(kc),
@@ -135,6 +159,9 @@ def topk(batch: Batch, scores: torch.Tensor, k: int, indices: Optional[torch.Ten
         indices = torch.empty((T, k), dtype=torch.int32, device=scores.device)
     if tuple(indices.shape) != (T, k):
         raise ValueError("indices must be [T, k]")
+    _rows(scores, "scores", batch)
+    if scores.dim() != 2 or scores.shape[1] < batch.max_seq_len:
+        raise ValueError("scores must be [T, ld] with ld >= max_seq_len")
     need = topk_workspace_size(batch.total_q, batch.max_seq_len, k)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
@@ -155,8 +182,9 @@ def page_scores(batch: Batch, scores: torch.Tensor, page_size: int,
     n_pages = max(1, -(-batch.max_seq_len // page_size))
     if out is None:
         out = torch.empty((T, n_pages), dtype=torch.float32, device=scores.device)
-    if out.dim() != 2 or out.shape[0] != T:
-        raise ValueError("page scores must be [T, ld_pages]")
+    if out.dim() != 2 or out.shape[0] != T or out.shape[1] < n_pages:
+        raise ValueError("page scores must be [T, ld_pages] with ld_pages >= the page count")
+    _rows(scores, "scores", batch)
     b = batch.c()
     check(lib.dsa_page_scores(ctypes.byref(b), _dev(scores, "scores", torch.float32),
                               scores.shape[1], page_size, _dev(out, "page_scores", torch.float32),
@@ -177,8 +205,9 @@ def indexer_page_scores(batch: Batch, q_idx: torch.Tensor, w: torch.Tensor, keys
     n_pages = max(1, -(-batch.max_seq_len // page_size))
     if out is None:
         out = torch.empty((T, n_pages), dtype=torch.float32, device=q_idx.device)
-    if out.dim() != 2 or out.shape[0] != T:
-        raise ValueError("page scores must be [T, ld_pages]")
+    if out.dim() != 2 or out.shape[0] != T or out.shape[1] < n_pages:
+        raise ValueError("page scores must be [T, ld_pages] with ld_pages >= the page count")
+    _rows(q_idx, "q_idx", batch)
     b, kc = batch.c(), keys.c()
     check(lib.dsa_indexer_page_scores(ctypes.byref(b), _dev(q_idx, "q_idx"), qd,
                                       _dev(w, "w", torch.float32), H, D, ctypes.byref(kc),
@@ -207,6 +236,7 @@ def page_topk(batch: Batch, page_scores: torch.Tensor, page_size: int, kp: int,
         raise ValueError("pages must be [T, kp]")
     if indices is not None and tuple(indices.shape) != (T, kp * page_size):
         raise ValueError("indices must be [T, kp * page_size]")
+    _rows(page_scores, "page_scores", batch)
     need = page_topk_workspace_size(batch.total_q, batch.max_seq_len, page_size, kp)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -234,11 +264,18 @@ def sparse_mla_fwd(batch: Batch, q: torch.Tensor, kv: PagedCache, indices: torch
     if qd not in (DSA_F32, DSA_BF16):
         raise TypeError("q must be float32 or bfloat16")
     d_rope = D - d_latent
+    if indices.dim() != 2:
+        raise ValueError("indices must be [T, k]")
     k = indices.shape[1]
+    _rows(q, "q", batch)
+    _rows(indices, "indices", batch)
     if out is None:
         out = torch.empty((T, H, d_latent), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _rows(out, "out", batch, (H, d_latent))
+    if lse is not None:
+        _rows(lse, "lse", batch, (H,))
     need = sparse_mla_workspace_size(batch.total_q, H, d_latent, k)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -279,12 +316,21 @@ def sparse_mla_fwd_layers(batch: Batch, qs: Sequence[torch.Tensor], kvs: Sequenc
     if any(tuple(q.shape) != (T, H, D) or q.dtype != qs[0].dtype for q in qs):
         raise ValueError("every layer's q must have the same shape and dtype")
     d_rope = D - d_latent
+    if indices.dim() != 2:
+        raise ValueError("indices must be [T, k]")
     k = indices.shape[1]
     dev = qs[0].device
+    _rows(qs[0], "q", batch)
+    _rows(indices, "indices", batch)
     if outs is None:
         outs = [torch.empty((T, H, d_latent), dtype=torch.float32, device=dev) for _ in range(n)]
     if lses is None and want_lse:
         lses = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in range(n)]
+    for o in outs:
+        _rows(o, "out", batch, (H, d_latent))
+    for x in lses or []:
+        if x is not None:
+            _rows(x, "lse", batch, (H,))
     need = sparse_mla_layers_workspace_size(n, batch.total_q, H, d_latent, k)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -3,7 +3,9 @@
     python sparse_attention_decode_lightning_amd/build.py
 
 Sources are compiled in parallel into ``_build/`` at the repository root and
-linked into ``sparse_attention_decode_lightning_amd/libdsa.so``.
+linked into ``sparse_attention_decode_lightning_amd/libdsa.so``. The
+benchmark's read-stream probe (``include/dsa_bench.h``) is linked on its own
+into ``libdsa_bench.so``: it is a measurement helper, not part of the path.
 """
 
 from __future__ import annotations
@@ -19,8 +21,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
+BENCH_LIB = os.path.join(PKG, "libdsa_bench.so")
 
 SOURCES = ["dsa_api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "kv_append.hip", "page_select.hip"]
+BENCH_SOURCES = ["bench_read.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
@@ -54,19 +58,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source for gfx950 and link libdsa.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source for gfx950, link libdsa.so and libdsa_bench.so; returns the
+    path of libdsa.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + BENCH_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in BENCH_SOURCES], BENCH_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {BENCH_LIB}")
     return LIB
 
 

@@ -158,7 +158,9 @@ dsa_status mla_layers(const dsa_batch *batch, int32_t n_layers, const void *cons
   if (bt.total_q > 0 && indices == nullptr) return DSA_ERR_NULL;
   if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
   if (n_heads < 1 || d_latent < 1 || d_rope < 0 || k < 1) return DSA_ERR_SHAPE;
-  if (!isfinite(scale)) return DSA_ERR_SHAPE;
+  // a softmax scale is positive (the pages tie it to 1 / sqrt(192 + 64)); the
+  // MFMA kernel takes a tile's maximum of the raw logits before scaling
+  if (!isfinite(scale) || !(scale > 0.0f)) return DSA_ERR_SHAPE;
   if (!aligned(indices, 4)) return DSA_ERR_SHAPE;
   dsa::MlaLayer ly[dsa::kMlaMaxLayers];
   for (int l = 0; l < n_layers; ++l) {

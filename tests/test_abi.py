@@ -28,6 +28,27 @@ def test_every_declared_symbol_is_exported():
     assert set(names) <= exported
 
 
+def test_bench_probe_library_exports_its_header():
+    """include/dsa_bench.h (the benchmark's read-stream probe) is exported by
+    libdsa_bench.so, and it rejects bad arguments before any launch."""
+    import re
+    text = open(os.path.join(ROOT, "include", "dsa_bench.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["dsa_bench_read", "dsa_bench_read_blocks"]
+    path = os.path.join(os.path.dirname(L.LIB_PATH), "libdsa_bench.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(names) <= exported
+    lib = ctypes.CDLL(path)
+    lib.dsa_bench_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    assert lib.dsa_bench_read(None, 16, FAKE, None) == 1
+    assert lib.dsa_bench_read(FAKE, 0, FAKE, None) == 1
+    assert lib.dsa_bench_read(FAKE + 4, 16, FAKE, None) == 2
+
+
 def test_abi_version_and_status_strings():
     assert L.lib.dsa_abi_version() == 1
     for code, name in L.STATUS_NAMES.items():
@@ -123,6 +144,7 @@ def _mla(b=None, q=FAKE, qd=L.DSA_BF16, H=64, DL=512, DR=64, c=None, idx=FAKE, k
     (dict(b=False), 1), (dict(q=None), 1), (dict(idx=None), 1), (dict(out=None), 1),
     (dict(c=False), 1),
     (dict(DR=32), 2), (dict(k=0), 2), (dict(scale=float("nan")), 2), (dict(H=0), 2),
+    (dict(scale=0.0), 2), (dict(scale=-0.0625), 2), (dict(scale=float("inf")), 2),
     (dict(out=FAKE + 4), 2),
     (dict(qd=L.DSA_F32), 3), (dict(c=_cache(row_elems=576, dtype=L.DSA_FP8_E4M3)), 3),
     (dict(ws=None), 4), (dict(wsb=16), 4),

@@ -1,9 +1,10 @@
 """GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
 
 Small cases are compared element by element (several tiles and ragged tails,
-every kernel variant); the five full-size workloads run in the launch
-configuration the benchmark times and are compared on sampled rows, with the
-index invariants checked on every row.
+every kernel variant); the full-size workloads run in the launch
+configuration the benchmark times and are compared on every row (every 64th
+row of the 4,096-row prefill chunk), with the index invariants checked on
+every row.
 """
 
 import numpy as np
@@ -50,6 +51,13 @@ SMALL_CASES = {
                                     topk=512, n_layers=1),
     "mla_generic_bf16": small_variant(BF16_DECODE, batch=2, lens=(300, 129), mla_heads=16,
                                       d_latent=128, d_rope=32, topk=100),
+    # 64-head MFMA MLA with k not a multiple of the 32-row tile: one split
+    # ending in a partial tile (k = 100), a single partial tile (k = 17), and
+    # many splits whose last one is one row short (k = 2047)
+    "mla_mfma_k100": small_variant(BF16_DECODE, batch=3, lens=(300, 1000, 77), topk=100),
+    "mla_mfma_k17": small_variant(BF16_DECODE, batch=3, lens=(300, 1000, 9), topk=17),
+    "mla_mfma_k2047": small_variant(BF16_DECODE, batch=2, lens=(3000, 2071), q_per_seq=(2, 1),
+                                    topk=2047),
 }
 
 
@@ -180,11 +188,13 @@ def test_mutated_metadata_is_detected(dev):
 
 
 FULL = ["decode_b32_l8k", "indexshare_b64", "prefill_q4k_l32k", "verify_b8_l240k"]
+# every row of the decode-shaped workloads; every 64th row of the 4,096-row
+# prefill chunk (its last row included)
 SAMPLE_ROWS = {
-    "decode_b32_l8k": [0, 13, 31],
-    "indexshare_b64": [0, 17, 40, 63],
-    "prefill_q4k_l32k": [0, 1, 777, 2048, 4095],
-    "verify_b8_l240k": [0, 3, 18, 31],
+    "decode_b32_l8k": list(range(32)),
+    "indexshare_b64": list(range(64)),
+    "prefill_q4k_l32k": list(range(0, 4096, 64)) + [4095],
+    "verify_b8_l240k": list(range(32)),
 }
 
 
