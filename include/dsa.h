@@ -221,6 +221,32 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const void *q, int32_t q_d
                               size_t workspace_bytes, void *stream);
 
 /*
+ * dsa_sparse_mla_fwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Identical arguments, results bit for bit and errors, except
+ * that there is no workspace argument: the split partials go to a static
+ * device array that the library owns, DSA_MLA_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the library's load on that GPU until the process ends. The call
+ * allocates and frees nothing.
+ *
+ * Limit: a call whose dsa_sparse_mla_workspace_size(total_q, n_heads,
+ * d_latent, k) exceeds DSA_MLA_NOALLOC_SCRATCH_BYTES returns
+ * DSA_ERR_WORKSPACE before anything is enqueued (at k = 2048 every batch
+ * size fits: the partials peak just under the limit at 255 query rows).
+ *
+ * All calls on one GPU share that GPU's array: calls that may overlap on one
+ * GPU (several streams, several host threads) race and give undefined
+ * results; calls ordered on one stream do not. The first call on a device
+ * looks up that device's copy of the array (the device current on the
+ * calling thread); DSA_ERR_LAUNCH if that lookup fails.
+ */
+#define DSA_MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dsa_status dsa_sparse_mla_fwd_noalloc(const dsa_batch *batch, const void *q, int32_t q_dtype,
+                                      int32_t n_heads, int32_t d_latent, int32_t d_rope,
+                                      const dsa_paged_cache *kv, const int32_t *indices, int32_t k,
+                                      float scale, float *out, float *lse, void *stream);
+
+/*
  * IndexShare over several layers in one call ("GLM-5.2 on vLLM Ascend:
  * Request-to-Backend Inference Path", section 7: one indexer's top-k is
  * reused by the attention of the layers that share it; "vLLM Inference Path:

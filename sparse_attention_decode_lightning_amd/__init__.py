@@ -33,6 +33,7 @@ __all__ = [
     "Batch", "PagedCache", "DSAError", "indexer_scores", "topk", "sparse_mla_fwd",
     "topk_workspace_size", "sparse_mla_workspace_size", "abi_version", "kv_append",
     "page_scores", "page_topk", "page_topk_workspace_size", "indexer_page_scores",
+    "sparse_mla_fwd_noalloc",
 ]
 
 _DT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.uint8: DSA_FP8_E4M3,
@@ -287,6 +288,34 @@ def sparse_mla_fwd(batch: Batch, q: torch.Tensor, kv: PagedCache, indices: torch
                                  float(scale), _dev(out, "out", torch.float32),
                                  0 if lse is None else _dev(lse, "lse", torch.float32), wp, wb,
                                  _stream(q.device)), "dsa_sparse_mla_fwd")
+    return out, lse
+
+
+def sparse_mla_fwd_noalloc(batch: Batch, q: torch.Tensor, kv: PagedCache, indices: torch.Tensor,
+                           d_latent: int, scale: float, out: torch.Tensor,
+                           lse: Optional[torch.Tensor] = None):
+    """sparse_mla_fwd with the split partials in the library's static per-GPU scratch
+    array instead of a workspace (dsa_sparse_mla_fwd_noalloc): the caller passes the
+    outputs, and neither the library nor this wrapper allocates. Calls that may overlap
+    on one GPU race on the shared array."""
+    T, H, D = q.shape
+    qd = _DT.get(q.dtype)
+    if qd not in (DSA_F32, DSA_BF16):
+        raise TypeError("q must be float32 or bfloat16")
+    if indices.dim() != 2:
+        raise ValueError("indices must be [T, k]")
+    k = indices.shape[1]
+    _rows(q, "q", batch)
+    _rows(indices, "indices", batch)
+    _rows(out, "out", batch, (H, d_latent))
+    if lse is not None:
+        _rows(lse, "lse", batch, (H,))
+    b, kc = batch.c(), kv.c()
+    check(lib.dsa_sparse_mla_fwd_noalloc(ctypes.byref(b), _dev(q, "q"), qd, H, d_latent, D - d_latent,
+                                         ctypes.byref(kc), _dev(indices, "indices", torch.int32), k,
+                                         float(scale), _dev(out, "out", torch.float32),
+                                         0 if lse is None else _dev(lse, "lse", torch.float32),
+                                         _stream(q.device)), "dsa_sparse_mla_fwd_noalloc")
     return out, lse
 
 

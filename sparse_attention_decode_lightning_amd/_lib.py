@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "dsa.h")
 
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
+DSA_MLA_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/dsa.h
 STATUS_NAMES = {
     0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_DTYPE",
     4: "DSA_ERR_WORKSPACE", 5: "DSA_ERR_UNSUPPORTED", 6: "DSA_ERR_LAUNCH",
@@ -74,6 +75,8 @@ def _load():
     lib.dsa_sparse_mla_workspace_size.argtypes = [I32, I32, I32, I32]
     lib.dsa_sparse_mla_fwd.restype = ctypes.c_int
     lib.dsa_sparse_mla_fwd.argtypes = [BP, P, I32, I32, I32, I32, CP, P, I32, F, P, P, P, SZ, P]
+    lib.dsa_sparse_mla_fwd_noalloc.restype = ctypes.c_int
+    lib.dsa_sparse_mla_fwd_noalloc.argtypes = [BP, P, I32, I32, I32, I32, CP, P, I32, F, P, P, P]
     lib.dsa_sparse_mla_layers_workspace_size.restype = SZ
     lib.dsa_sparse_mla_layers_workspace_size.argtypes = [I32, I32, I32, I32, I32]
     lib.dsa_sparse_mla_fwd_layers.restype = ctypes.c_int

@@ -149,7 +149,7 @@ dsa_status mla_layers(const dsa_batch *batch, int32_t n_layers, const void *cons
                       int32_t q_dtype, int32_t n_heads, int32_t d_latent, int32_t d_rope,
                       const dsa_paged_cache *kv, const int32_t *indices, int32_t k, float scale,
                       float *const *out, float *const *lse, void *workspace,
-                      size_t workspace_bytes, void *stream) {
+                      size_t workspace_bytes, void *stream, bool use_scratch = false) {
   BatchArgs bt;
   dsa_status st = check_batch(batch, &bt);
   if (st != DSA_OK) return st;
@@ -182,9 +182,19 @@ dsa_status mla_layers(const dsa_batch *batch, int32_t n_layers, const void *cons
   if (!mfma_shape && d_latent > 1024) return DSA_ERR_UNSUPPORTED;
   if (mfma_shape && k > dsa::mla_max_k()) return DSA_ERR_UNSUPPORTED;
   const size_t need = (size_t)n_layers * dsa::mla_workspace_bytes(bt.total_q, n_heads, d_latent, k);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+  if (use_scratch) {
+    // the library's static scratch array stands in for the workspace
+    if (need > DSA_MLA_NOALLOC_SCRATCH_BYTES) return DSA_ERR_WORKSPACE;
+  } else if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
+                          !aligned(workspace, 16))) {
     return DSA_ERR_WORKSPACE;
+  }
   if (bt.total_q == 0) return DSA_OK;
+  if (use_scratch && need > 0) {
+    // this device's copy of the array (found on the first call on the device)
+    if (dsa::mla_scratch(&workspace) != hipSuccess) return DSA_ERR_LAUNCH;
+    workspace_bytes = DSA_MLA_NOALLOC_SCRATCH_BYTES;
+  }
   return launch_status(dsa::launch_sparse_mla(bt, ly, n_layers, q_dtype, n_heads, d_latent,
                                               d_rope, indices, k, scale, workspace,
                                               workspace_bytes, static_cast<hipStream_t>(stream)));
@@ -217,6 +227,14 @@ dsa_status dsa_sparse_mla_fwd_layers(const dsa_batch *batch, int32_t n_layers,
                                      size_t workspace_bytes, void *stream) {
   return mla_layers(batch, n_layers, q, q_dtype, n_heads, d_latent, d_rope, kv, indices, k, scale,
                     out, lse, workspace, workspace_bytes, stream);
+}
+
+dsa_status dsa_sparse_mla_fwd_noalloc(const dsa_batch *batch, const void *q, int32_t q_dtype,
+                                      int32_t n_heads, int32_t d_latent, int32_t d_rope,
+                                      const dsa_paged_cache *kv, const int32_t *indices, int32_t k,
+                                      float scale, float *out, float *lse, void *stream) {
+  return mla_layers(batch, 1, &q, q_dtype, n_heads, d_latent, d_rope, kv, indices, k, scale, &out,
+                    &lse, nullptr, 0, stream, /*use_scratch=*/true);
 }
 
 dsa_status dsa_indexer_page_scores(const dsa_batch *batch, const void *q_idx, int32_t q_dtype,

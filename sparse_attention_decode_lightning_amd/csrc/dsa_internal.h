@@ -67,6 +67,9 @@ int mla_num_splits(int32_t total_q, int32_t n_heads, int32_t d_latent, int32_t k
 int mla_max_k();  // largest k of the 64-head bf16 MFMA path
 // workspace of one layer; a call over n layers needs n times this
 size_t mla_workspace_bytes(int32_t total_q, int32_t n_heads, int32_t d_latent, int32_t k);
+// Device address of the calling thread's current GPU's copy of the library's
+// static MLA scratch array (DSA_MLA_NOALLOC_SCRATCH_BYTES), found once per device.
+hipError_t mla_scratch(void **ptr);
 hipError_t launch_sparse_mla(const BatchArgs &bt, const MlaLayer *layers, int n_layers,
                              int32_t q_dtype, int32_t n_heads, int32_t d_latent, int32_t d_rope,
                              const int32_t *indices, int32_t k, float scale, void *workspace,

@@ -38,10 +38,19 @@
 //    (workgroups are dispatched round-robin over the 8 XCDs), so the row's
 //    query block is fetched from HBM once and then served by that XCD's L2.
 //  * Splits of a row are merged by a log-sum-exp combine kernel.
+#include <mutex>
 #include <type_traits>
 
 #include "dsa_device.h"
 #include "dsa_internal.h"
+
+// Library-owned workspace of dsa_sparse_mla_fwd_noalloc, for callers that
+// cannot allocate: the split partials of one call, at most
+// DSA_MLA_NOALLOC_SCRATCH_BYTES. Every GPU that loads this code holds its own
+// copy (zero-filled at load) until the process ends. In host code `scratch`
+// names a host-side stand-in, never a device address: the device address of
+// each GPU's copy comes from hipGetSymbolAddress (dsa::mla_scratch below).
+static __device__ __align__(256) uint8_t scratch[DSA_MLA_NOALLOC_SCRATCH_BYTES];
 
 namespace dsa {
 namespace {
@@ -760,6 +769,30 @@ int mla_num_splits(int32_t total_q, int32_t n_heads, int32_t d_latent, int32_t k
 }
 
 int mla_max_k() { return kMaxSplits * kMaxRowsPerSplit; }
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once found
+}  // namespace
+
+hipError_t mla_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // with `dev` current: this GPU's copy of the array
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t mla_workspace_bytes(int32_t total_q, int32_t n_heads, int32_t d_latent, int32_t k) {
   const int s = mla_num_splits(total_q, n_heads, d_latent, k);

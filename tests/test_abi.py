@@ -154,6 +154,35 @@ def test_mla_rejects_bad_arguments(kw, code):
     assert _mla(**kw) == code
 
 
+def _mla_noalloc(b=None, q=FAKE, qd=L.DSA_BF16, H=64, DL=512, DR=64, c=None, idx=FAKE, k=2048,
+                 scale=0.0625, out=FAKE, lse=FAKE):
+    b = _batch() if b is None else b
+    c = _cache(row_elems=576) if c is None else c
+    return L.lib.dsa_sparse_mla_fwd_noalloc(ctypes.byref(b) if b is not False else None, q, qd, H,
+                                            DL, DR, ctypes.byref(c) if c is not False else None,
+                                            idx, k, scale, out, lse, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=False), 1), (dict(q=None), 1), (dict(idx=None), 1), (dict(out=None), 1),
+    (dict(c=False), 1), (dict(DR=32), 2), (dict(k=0), 2), (dict(scale=0.0), 2),
+    (dict(out=FAKE + 4), 2), (dict(qd=L.DSA_F32), 3),
+    # partials beyond the static scratch array: 32 rows x 32 splits x 64 x 514 fp32
+    (dict(b=_batch(batch=32, total_q=32, max_q=1, max_seq_len=70000, bt_stride=1100),
+          k=65536), 4),
+])
+def test_mla_noalloc_rejects_bad_arguments(kw, code):
+    """The allocation-free variant validates like dsa_sparse_mla_fwd and rejects a call
+    whose partials would not fit the library's scratch array, before any HIP call."""
+    assert _mla_noalloc(**kw) == code
+
+
+def test_mla_noalloc_limit_covers_every_decode_batch_at_k2048():
+    assert max(L.lib.dsa_sparse_mla_workspace_size(t, 64, 512, 2048) for t in range(1, 1025)) \
+        <= L.DSA_MLA_NOALLOC_SCRATCH_BYTES
+    assert L.lib.dsa_sparse_mla_workspace_size(32, 64, 512, 65536) > L.DSA_MLA_NOALLOC_SCRATCH_BYTES
+
+
 def test_workspace_sizes_are_pure_functions_of_bounds():
     assert L.lib.dsa_topk_workspace_size(32, 8192, 2048) == 0
     # rows over 32K: keys and positions of k survivors per chunk (16K positions,
