@@ -59,6 +59,13 @@ TOPK_CASES = [
     ((300000, 140000), 2048),
     ((100000, 50000), 8192),
     ((5000, 64), 64),
+    # rows shorter than one wave with k below the row length, on the 256-thread
+    # paths (one and four keys per thread) and the 1024-thread one: lanes past
+    # the row take part in the block maximum with key 0
+    ((47, 30, 63), 20),
+    ((47, 200, 900), 20),
+    ((47, 1000, 3000), 20),
+    ((47, 5), 1),
 ]
 
 
