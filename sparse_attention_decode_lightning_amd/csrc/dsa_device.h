@@ -123,6 +123,31 @@ struct RowInfo {
   int t;  // absolute position of the row; -1 if the metadata leaves it none
 };
 
+// The clamping half of row_info, shared with host-side checks: sequence b
+// (already found) with query offsets c0 = cu_q[b], c1 = cu_q[b + 1] and
+// length len, as read from memory. Offsets are clamped into [0, total_q],
+// the length into [0, max_seq_len], and the position to at most L - 1, so
+// that whatever the metadata holds, t is -1 or in [0, max_seq_len).
+__host__ __device__ inline int clamp_int(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+__host__ __device__ inline RowInfo row_clamp(int b, int c0, int c1, int len, int total_q,
+                                             int max_seq_len, int row) {
+  RowInfo ri;
+  ri.b = b;
+  const int q0 = clamp_int(c0, 0, total_q);
+  const int q1 = clamp_int(c1, q0, total_q);
+  const int L = clamp_int(len, 0, max_seq_len);
+  const int t = L - (q1 - q0) + (row - q0);
+  ri.t = (row < q0 || row >= q1) ? -1 : (t < L - 1 ? t : L - 1);
+  ri.t = ri.t < -1 ? -1 : ri.t;
+  return ri;
+}
+
+// A physical page id from a block table, clamped into the pool [0, num_pages).
+__host__ __device__ inline int64_t clamp_page(int64_t page, int64_t num_pages) {
+  return page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+}
+
 // Sequence and causal position of a flattened query row: b is the largest
 // b < batch with cu_q[b] <= row (0 if none). Wave-cooperative: every lane of
 // the wave must be active and pass the same row. With non-decreasing offsets
@@ -153,23 +178,14 @@ __device__ __forceinline__ RowInfo row_info(const int32_t *cu_q, const int32_t *
     }
     if (hit != ~0ull) break;
   }
-  RowInfo ri;
-  ri.b = b;
-  const int q0 = min(max(c0, 0), total_q);
-  const int q1 = min(max(c1, q0), total_q);
-  const int L = min(max(len, 0), max_seq_len);
-  const int t = L - (q1 - q0) + (row - q0);
-  ri.t = (row < q0 || row >= q1) ? -1 : min(t, L - 1);
-  ri.t = ri.t < -1 ? -1 : ri.t;
-  return ri;
+  return row_clamp(b, c0, c1, len, total_q, max_seq_len, row);
 }
 
 // Element offset of token `pos` of sequence `b` in a paged cache, with the
 // physical page id clamped into the pool so malformed tables stay in bounds.
 __device__ __forceinline__ int64_t paged_row(const int32_t *block_table, int64_t bt_stride, int b,
                                              int pos, int page_size, int64_t num_pages) {
-  int64_t page = block_table[(int64_t)b * bt_stride + pos / page_size];
-  page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+  const int64_t page = clamp_page(block_table[(int64_t)b * bt_stride + pos / page_size], num_pages);
   return page * page_size + pos % page_size;
 }
 

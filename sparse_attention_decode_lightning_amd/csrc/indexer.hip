@@ -290,8 +290,7 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
   auto copy_block = [&](int blk) {
     const int kb0 = key0 + blk * kStreamKeys;
     const int pidx = (int)fast_div((uint32_t)kb0, pdiv);
-    int64_t page = block_table[bt_row + pidx];
-    page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+    const int64_t page = dsa::clamp_page(block_table[bt_row + pidx], num_pages);
     const int64_t row0 = page * page_size + (kb0 - pidx * page_size);
     const uint8_t *base = kdata + row0 * RB;
     const lds_u8 *st = (const lds_u8 *)s_st[blk % kStreamStages];
@@ -569,9 +568,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
   u32x4_t stage[kPfStage];
   int btv[kPfStage];
   auto key_pos = [&](int blk, int i) { return min(kbeg + blk * kPfKeys + kr0 + 32 * i, t_last); };
-  auto clamp_page = [&](int64_t page) {
-    return page < 0 ? (int64_t)0 : (page >= num_pages ? num_pages - 1 : page);
-  };
+  auto clamp_page = [&](int64_t page) { return dsa::clamp_page(page, num_pages); };
   auto bt_load = [&](int blk) {
     if constexpr (CONTIG) {
       btv[0] = block_table[bt_row + (int)fast_div((uint32_t)(kbeg + blk * kPfKeys), pdiv)];

@@ -293,9 +293,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     }
     page0 = bt_row[0];
   }
-  auto clamp_page = [&](int64_t pg) -> uint32_t {
-    return (uint32_t)(pg < 0 ? 0 : (pg >= num_pages ? num_pages - 1 : pg));
-  };
+  auto clamp_page = [&](int64_t pg) -> uint32_t { return (uint32_t)dsa::clamp_page(pg, num_pages); };
   const uint32_t safe_row = clamp_page(page0) * (uint32_t)page_size;
 #pragma unroll
   for (int e = 0; e < kEntries; ++e) {
