@@ -279,6 +279,40 @@ dsa_status dsa_sparse_mla_fwd_layers(const dsa_batch *batch, int32_t n_layers,
                                      size_t workspace_bytes, void *stream);
 
 /*
+ * Query-blocked sparse MLA ("Making GLM-5.2 Sparse on TPUs", section "Reuse
+ * pages across queries": a block of queries loads the union of its selected
+ * rows once, and a membership mask restores each query's own selection
+ * before the softmax). The same operation as dsa_sparse_mla_fwd on the same
+ * arguments; only the order of the fp32 sums differs, so results agree to
+ * rounding, not bit for bit.
+ *
+ * Query rows are taken in blocks of QB consecutive rows (QB = 4 for 16 or
+ * more heads, 8 for 8 heads), and each block's selections are merged into one
+ * list of physical rows with a membership mask per row. Every row of the
+ * list is loaded once per block and group of 64 / QB heads, and feeds 64
+ * (query, head) pairs. This pays when the block's queries select overlapping
+ * rows, or when a query has fewer than 64 heads (a head-sharded layer); when
+ * they share nothing, it costs about QB times the logit work of the
+ * per-query call. The merge needs each row's valid entries (positions in
+ * [0, t_r]) first and strictly ascending, as dsa_topk and dsa_page_topk write
+ * them, and the block's rows in one sequence; any other block is attended to
+ * as given, each entry counted once per occurrence, like dsa_sparse_mla_fwd.
+ *
+ * Arguments as for dsa_sparse_mla_fwd; the workspace holds the unions.
+ *   workspace  device, >= dsa_sparse_mla_qblocked_workspace_size(total_q, n_heads, k)
+ *
+ * Supported: bf16, d_latent 512, d_rope 64, n_heads 8 or 16, 32, 48, 64, QB * k
+ * <= 16384, max_seq_len < 2^29 and fewer than 2^32 rows in the cache;
+ * otherwise DSA_ERR_UNSUPPORTED. Other errors as for dsa_sparse_mla_fwd.
+ */
+size_t dsa_sparse_mla_qblocked_workspace_size(int32_t total_q, int32_t n_heads, int32_t k);
+dsa_status dsa_sparse_mla_fwd_qblocked(const dsa_batch *batch, const void *q, int32_t q_dtype,
+                                       int32_t n_heads, int32_t d_latent, int32_t d_rope,
+                                       const dsa_paged_cache *kv, const int32_t *indices, int32_t k,
+                                       float scale, float *out, float *lse, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
+/*
  * Page scores for page-budget selection, the alternative to token top-k that
  * bounds the pages attention reads ("Making GLM-5.2 Sparse on TPUs", section
  * "Make the sparsity unit match the memory unit": a page is ranked by its

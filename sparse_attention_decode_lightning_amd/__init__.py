@@ -33,7 +33,7 @@ __all__ = [
     "Batch", "PagedCache", "DSAError", "indexer_scores", "topk", "sparse_mla_fwd",
     "topk_workspace_size", "sparse_mla_workspace_size", "abi_version", "kv_append",
     "page_scores", "page_topk", "page_topk_workspace_size", "indexer_page_scores",
-    "sparse_mla_fwd_noalloc",
+    "sparse_mla_fwd_noalloc", "sparse_mla_fwd_qblocked", "sparse_mla_qblocked_workspace_size",
 ]
 
 _DT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.uint8: DSA_FP8_E4M3,
@@ -316,6 +316,48 @@ def sparse_mla_fwd_noalloc(batch: Batch, q: torch.Tensor, kv: PagedCache, indice
                                          float(scale), _dev(out, "out", torch.float32),
                                          0 if lse is None else _dev(lse, "lse", torch.float32),
                                          _stream(q.device)), "dsa_sparse_mla_fwd_noalloc")
+    return out, lse
+
+
+def sparse_mla_qblocked_workspace_size(total_q: int, n_heads: int, k: int) -> int:
+    return int(lib.dsa_sparse_mla_qblocked_workspace_size(total_q, n_heads, k))
+
+
+def sparse_mla_fwd_qblocked(batch: Batch, q: torch.Tensor, kv: PagedCache, indices: torch.Tensor,
+                            d_latent: int, scale: float, out: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """Query-blocked sparse MLA (dsa_sparse_mla_fwd_qblocked): the same result as
+    sparse_mla_fwd to rounding, each block of query rows loading the union of its
+    selected rows once. Returns (out [T, H, d_latent], lse [T, H] or None)."""
+    T, H, D = q.shape
+    qd = _DT.get(q.dtype)
+    if qd not in (DSA_F32, DSA_BF16):
+        raise TypeError("q must be float32 or bfloat16")
+    if indices.dim() != 2:
+        raise ValueError("indices must be [T, k]")
+    k = indices.shape[1]
+    _rows(q, "q", batch)
+    _rows(indices, "indices", batch)
+    if out is None:
+        out = torch.empty((T, H, d_latent), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _rows(out, "out", batch, (H, d_latent))
+    if lse is not None:
+        _rows(lse, "lse", batch, (H,))
+    need = sparse_mla_qblocked_workspace_size(batch.total_q, H, k)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wp = 0 if workspace is None else _dev(workspace, "workspace")
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    b, kc = batch.c(), kv.c()
+    check(lib.dsa_sparse_mla_fwd_qblocked(ctypes.byref(b), _dev(q, "q"), qd, H, d_latent,
+                                          D - d_latent, ctypes.byref(kc),
+                                          _dev(indices, "indices", torch.int32), k, float(scale),
+                                          _dev(out, "out", torch.float32),
+                                          0 if lse is None else _dev(lse, "lse", torch.float32),
+                                          wp, wb, _stream(q.device)), "dsa_sparse_mla_fwd_qblocked")
     return out, lse
 
 

@@ -77,6 +77,11 @@ def _load():
     lib.dsa_sparse_mla_fwd.argtypes = [BP, P, I32, I32, I32, I32, CP, P, I32, F, P, P, P, SZ, P]
     lib.dsa_sparse_mla_fwd_noalloc.restype = ctypes.c_int
     lib.dsa_sparse_mla_fwd_noalloc.argtypes = [BP, P, I32, I32, I32, I32, CP, P, I32, F, P, P, P]
+    lib.dsa_sparse_mla_qblocked_workspace_size.restype = SZ
+    lib.dsa_sparse_mla_qblocked_workspace_size.argtypes = [I32, I32, I32]
+    lib.dsa_sparse_mla_fwd_qblocked.restype = ctypes.c_int
+    lib.dsa_sparse_mla_fwd_qblocked.argtypes = [BP, P, I32, I32, I32, I32, CP, P, I32, F, P, P, P,
+                                                SZ, P]
     lib.dsa_sparse_mla_layers_workspace_size.restype = SZ
     lib.dsa_sparse_mla_layers_workspace_size.argtypes = [I32, I32, I32, I32, I32]
     lib.dsa_sparse_mla_fwd_layers.restype = ctypes.c_int

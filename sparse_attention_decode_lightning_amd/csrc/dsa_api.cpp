@@ -237,6 +237,47 @@ dsa_status dsa_sparse_mla_fwd_noalloc(const dsa_batch *batch, const void *q, int
                     &lse, nullptr, 0, stream, /*use_scratch=*/true);
 }
 
+size_t dsa_sparse_mla_qblocked_workspace_size(int32_t total_q, int32_t n_heads, int32_t k) {
+  return dsa::mla_qblock_workspace_bytes(total_q, n_heads, k);
+}
+
+dsa_status dsa_sparse_mla_fwd_qblocked(const dsa_batch *batch, const void *q, int32_t q_dtype,
+                                       int32_t n_heads, int32_t d_latent, int32_t d_rope,
+                                       const dsa_paged_cache *kv, const int32_t *indices, int32_t k,
+                                       float scale, float *out, float *lse, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+  BatchArgs bt;
+  dsa_status st = check_batch(batch, &bt);
+  if (st != DSA_OK) return st;
+  if (kv == nullptr) return DSA_ERR_NULL;
+  if (bt.total_q > 0 && (q == nullptr || out == nullptr || indices == nullptr)) return DSA_ERR_NULL;
+  if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (n_heads < 1 || d_latent < 1 || d_rope < 0 || k < 1) return DSA_ERR_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.0f)) return DSA_ERR_SHAPE;
+  dsa::MlaLayer ly;
+  st = check_cache(kv, bt, &ly.kv);
+  if (st != DSA_OK) return st;
+  if (ly.kv.dtype != q_dtype) return DSA_ERR_DTYPE;
+  if ((int64_t)ly.kv.row_elems != (int64_t)d_latent + d_rope) return DSA_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(indices, 4) ||
+      (lse != nullptr && !aligned(lse, 4)))
+    return DSA_ERR_SHAPE;
+  // positions and physical rows travel as 32-bit words in the unions
+  if (!dsa::mla_qblock_supported(q_dtype, n_heads, d_latent, d_rope, k) ||
+      bt.max_seq_len >= (1 << 29) ||
+      (uint64_t)ly.kv.num_pages * (uint64_t)ly.kv.page_size > 0xFFFFFFFFull)
+    return DSA_ERR_UNSUPPORTED;
+  const size_t need = dsa::mla_qblock_workspace_bytes(bt.total_q, n_heads, k);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+    return DSA_ERR_WORKSPACE;
+  if (bt.total_q == 0) return DSA_OK;
+  ly.q = q;
+  ly.out = out;
+  ly.lse = lse;
+  return launch_status(dsa::launch_sparse_mla_qblocked(bt, ly, n_heads, indices, k, scale, workspace,
+                                                       static_cast<hipStream_t>(stream)));
+}
+
 dsa_status dsa_indexer_page_scores(const dsa_batch *batch, const void *q_idx, int32_t q_dtype,
                                    const float *w, int32_t n_heads, int32_t head_dim,
                                    const dsa_paged_cache *keys, int32_t page_size,

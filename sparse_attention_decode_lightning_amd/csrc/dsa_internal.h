@@ -75,6 +75,16 @@ hipError_t launch_sparse_mla(const BatchArgs &bt, const MlaLayer *layers, int n_
                              const int32_t *indices, int32_t k, float scale, void *workspace,
                              size_t ws_bytes, hipStream_t stream);
 
+// Query-blocked sparse MLA (bf16, 512 + 64; 8 heads, or 16 to 64 in groups
+// of 16): the union of each block of query rows, then attention over it.
+int mla_qblock_qb(int32_t n_heads);  // query rows per block
+bool mla_qblock_supported(int32_t q_dtype, int32_t n_heads, int32_t d_latent, int32_t d_rope,
+                          int32_t k);
+size_t mla_qblock_workspace_bytes(int32_t total_q, int32_t n_heads, int32_t k);
+hipError_t launch_sparse_mla_qblocked(const BatchArgs &bt, const MlaLayer &layer, int32_t n_heads,
+                                      const int32_t *indices, int32_t k, float scale,
+                                      void *workspace, hipStream_t stream);
+
 hipError_t launch_page_scores(const BatchArgs &bt, const float *scores, int64_t ld,
                               int32_t page_size, float *page_scores, int64_t ld_pages,
                               hipStream_t stream);

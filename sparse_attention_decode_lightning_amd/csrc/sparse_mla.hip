@@ -43,6 +43,7 @@
 
 #include "dsa_device.h"
 #include "dsa_internal.h"
+#include "dsa_select.h"
 
 // Library-owned workspace of dsa_sparse_mla_fwd_noalloc, for callers that
 // cannot allocate: the split partials of one call, at most
@@ -92,6 +93,7 @@ __device__ __forceinline__ int chunk_swz(int c, int r) {
 }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short __attribute__((address_space(3))) *lds_i16_ptr;
@@ -198,6 +200,212 @@ struct MlaLayerArgs {
   float *out[kMlaMaxLayers];
   float *lse[kMlaMaxLayers];
 };
+
+// Direct copies of a wave's eight rows of a row tile into an LDS stage.
+// Instruction n of wave wv moves chunks 64n..64n+63 of the 576 chunks of rows
+// 8wv..8wv+7; lane l's chunk is row 8wv + (64n+l)/72, stored chunk
+// (64n+l)%72, fetched from that row's chunk chunk_swz(., row). The row is one
+// of two known to the instruction: 64n/72, or the next from lane
+// 72(64n/72 + 1) - 64n on. goff[n] holds the chunk's byte offset in its row,
+// less the 1024 (n % 4) that the copy's instruction offset adds back (plus
+// 3072 on the 32-bit path, whose base sits 3072 bytes below the cache so that
+// every offset stays non-negative). Row ids carry kInvalid as a flag, which
+// the copy strips (a flagged slot's row is a valid stand-in).
+template <bool kOff32>
+struct TileGather {
+  static constexpr uint32_t kBias = kOff32 ? 3072u : 0u;
+  uint32_t goff[kGatherInsts];
+  const uint8_t *kv;
+  uint32_t lds_wave;  // this wave's part of stage 0
+  int lane;
+
+  __device__ __forceinline__ TileGather(const uint8_t *kv_, uint32_t lds_tiles, int wv, int lane_)
+      : kv(kv_), lds_wave(lds_tiles + 8 * wv * kRowBytes), lane(lane_) {
+#pragma unroll
+    for (int n = 0; n < kGatherInsts; ++n) {
+      const int qc = 64 * n + lane;
+      const int rl = qc / 72, lc = qc % 72;
+      goff[n] = (uint32_t)(16 * chunk_swz(lc, 8 * wv + rl)) + kBias - 1024u * (n % 4);
+    }
+  }
+
+  __device__ __forceinline__ void copy(int stage, const u32x4_t ra, const u32x4_t rb) const {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_wave + (uint32_t)stage * kTileBytes);
+    const uint32_t rid[8] = {ra.x & ~kInvalid, ra.y & ~kInvalid, ra.z & ~kInvalid, ra.w & ~kInvalid,
+                             rb.x & ~kInvalid, rb.y & ~kInvalid, rb.z & ~kInvalid, rb.w & ~kInvalid};
+    if constexpr (kOff32) {
+      uint32_t v[kGatherInsts];
+#pragma unroll
+      for (int n = 0; n < kGatherInsts; ++n) {
+        const int q0 = (64 * n) / 72;
+        const int split_lane = 72 * (q0 + 1) - 64 * n;
+        const uint32_t r = (q0 == 7 || lane < split_lane) ? rid[q0] : rid[q0 + 1];
+        v[n] = __umul24(r, (uint32_t)kRowBytes) + goff[n];
+      }
+      lds_copy9(kv - kBias, v, lds);
+    } else {
+      uint64_t v[kGatherInsts];
+#pragma unroll
+      for (int n = 0; n < kGatherInsts; ++n) {
+        const int q0 = (64 * n) / 72;
+        const int split_lane = 72 * (q0 + 1) - 64 * n;
+        const uint32_t r = (q0 == 7 || lane < split_lane) ? rid[q0] : rid[q0 + 1];
+        v[n] = (uint64_t)((int64_t)(uintptr_t)kv + (int64_t)r * kRowBytes + (int32_t)goff[n]);
+      }
+      lds_copy9(v, lds);
+    }
+  }
+};
+
+// Per-lane operand offsets inside a row tile (loop-invariant), for lane
+// (g, j) of a wave: logits A operand: lane (g, i) reads tile row
+// tile_row(0, i), chunk 4s + g (M-tile 1 is 16 rows further with the same
+// permutation); latent steps s use a_lat[s & 3] plus 256 (s >> 2), the two
+// RoPE steps a_rope[s - 16]. Value operand: transposed read L covers rows
+// tile_row(L, 4g + j / 4), dims 4(j & 3) .. +4 of the 16-dim tile nt, which
+// uses v_off[nt & 7] plus 256 (nt >> 3); read L = 1 is 16 rows further.
+// lrow[m][r]: the tile row of this lane's logit (m, r), tile_row(m, 4g + r).
+struct TileLane {
+  uint32_t a_lat[4], a_rope[2];
+  uint32_t v_off[8];
+  int lrow[2][4];
+};
+
+__device__ __forceinline__ TileLane tile_lane(int g, int j) {
+  TileLane tl;
+  const int ar = tile_row(0, j);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) tl.a_lat[s] = ar * kRowBytes + 16 * chunk_swz(4 * s + g, ar);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) tl.a_rope[s] = ar * kRowBytes + 16 * chunk_swz(64 + 4 * s + g, ar);
+  const int vr = tile_row(0, 4 * g + (j >> 2));
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    tl.v_off[c] = vr * kRowBytes + 16 * ((2 * c + ((j & 3) >> 1)) ^ (vr & 15)) + 8 * (j & 1);
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tl.lrow[m][r] = tile_row(m, 4 * g + r);
+  return tl;
+}
+
+// One 32-row tile of the attention for the calling wave's 16 columns (a
+// column is one (query, head) pair; its query block is the B operand qf):
+// logits, softmax against the running reference, and PV into o. Bit r of
+// vmask (per lane: the tile's valid rows for this lane's column) masks tile
+// row r. The wave's restart flag is written to *over_flag.
+__device__ __forceinline__ void mla_tile(const lds_u8 *tb, uint32_t vmask, const TileLane &tl,
+                                         const u32x4_t (&qf)[kSteps], f32x4_t (&o)[32],
+                                         float &m_run, float &l_run, bool &overflow,
+                                         float scale_log2, int *over_flag) {
+  // logits (transposed): acc[m][r] = S[column j][row lrow[m][r]], A
+  // operands read one k-step ahead of the MFMAs
+  f32x4_t acc[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+  auto a_off = [&](int s_) -> uint32_t {
+    return s_ < 16 ? tl.a_lat[s_ & 3] + 256 * (s_ >> 2) : tl.a_rope[s_ - 16];
+  };
+  // A operands run kAhead k-steps ahead of their MFMAs
+  constexpr int kAhead = 4;
+  u32x4_t abuf[kSteps][2];
+#pragma unroll
+  for (int s_ = 0; s_ < kAhead; ++s_)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+      abuf[s_][m] = *(const __attribute__((address_space(3))) u32x4_t *)(tb + a_off(s_) + m * 16 * kRowBytes);
+#pragma unroll
+  for (int s_ = 0; s_ < kSteps; ++s_) {
+    if (s_ + kAhead < kSteps) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        abuf[s_ + kAhead][m] = *(const __attribute__((address_space(3))) u32x4_t *)(
+            tb + a_off(s_ + kAhead) + m * 16 * kRowBytes);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) acc[m] = mfma_16x16x32_bf16(abuf[s_][m], qf[s_], acc[m]);
+  }
+  // issue order: 2 * kAhead operand reads, then one read per MFMA
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+  for (int i = 0; i < 2 * (kSteps - kAhead); ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
+
+  // Value operands (transposed reads, two per 16-dim tile nt) run kVAhead
+  // tiles ahead of their MFMAs; the first kVAhead go out before the softmax
+  // so their latency hides under it.
+  auto vread = [&](int nt) -> u32x4_t {
+    const lds_u8 *vp = tb + tl.v_off[nt & 7] + 256 * (nt >> 3);
+    const uint2 v0 = lds_read_tr16(vp);
+    const uint2 v1 = lds_read_tr16(vp + 16 * kRowBytes);
+    return u32x4_t{v0.x, v0.y, v1.x, v1.y};
+  };
+  constexpr int kVAhead = 6;
+  u32x4_t vbuf[32];
+#pragma unroll
+  for (int nt = 0; nt < kVAhead; ++nt) vbuf[nt] = vread(nt);
+  __builtin_amdgcn_sched_barrier(0);
+  if (vmask != 0xFFFFFFFFu) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (!((vmask >> tl.lrow[m][r]) & 1u)) acc[m][r] = -INFINITY;
+  }
+  // softmax of column j in base 2 against a reference maximum m_run
+  // fixed by the head's first valid tile: p = 2^(x - m_run). A later tile
+  // may exceed it by up to kHeadroom (p <= 2^kHeadroom keeps every sum
+  // finite); beyond that the whole split restarts with a higher reference,
+  // so the accumulated output is never rescaled in the loop.
+  float mx = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
+                   fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
+  mx = group4_max(mx) * scale_log2;
+  m_run = m_run == -INFINITY ? mx : m_run;
+  const bool over = mx > m_run + kHeadroom;
+  m_run = over ? mx : m_run;  // per lane: a restarted pass starts from here
+  overflow |= over;
+  // every lane writes the same word, so no branch splits the tile's code;
+  // the flag is read by all waves after the next barrier (a restarted
+  // split discards whatever this tile accumulates)
+  *over_flag = __ballot(overflow) != 0ull ? 1 : 0;
+  // until the head's first valid row every logit is -inf: subtract 0, not -inf
+  const float m_sub = m_run == -INFINITY ? 0.0f : m_run;
+  float p[2][4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[m][r] = fast_exp2(fmaf(acc[m][r], scale_log2, -m_sub));
+      l_run += p[m][r];
+    }
+  // P as the A operand of PV: head j, k-slots 8g + 4m + r <-> rows lrow[m][r].
+  // p = hi + lo in bf16 to 2^-16 relative: bf16 rounding of p alone (2^-9)
+  // is too coarse for rows that attend to only a few positions.
+  u32x4_t pa, pl;
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t hi = pack_bf16x2(p[m][2 * h], p[m][2 * h + 1]);
+      const float r0 = p[m][2 * h] - __uint_as_float(hi << 16);
+      const float r1 = p[m][2 * h + 1] - __uint_as_float(hi & 0xFFFF0000u);
+      pa[2 * m + h] = hi;
+      pl[2 * m + h] = pack_bf16x2(r0, r1);
+    }
+  // PV in a fixed order: each pair of MFMAs is preceded by the reads of
+  // the tile kVAhead further on. (Left to itself the scheduler sinks every
+  // read to just before its MFMAs, which exposes the whole LDS latency once
+  // per pair.)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int nt = 0; nt < 32; ++nt) {
+    if (nt + kVAhead < 32) vbuf[nt + kVAhead] = vread(nt + kVAhead);
+    o[nt] = mfma_16x16x32_bf16(pa, vbuf[nt], o[nt]);
+    o[nt] = mfma_16x16x32_bf16(pl, vbuf[nt], o[nt]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
 
 template <bool kOff32>
 __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
@@ -313,26 +521,9 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     }
   }
 
-  typedef __attribute__((address_space(3))) uint8_t lds_u8;
   const lds_u8 *tiles = (const lds_u8 *)s_tiles;
   const uint32_t lds_tiles = (uint32_t)(uintptr_t)tiles;
-  // Gather map: instruction n of wave wv moves chunks 64n..64n+63 of the 576
-  // chunks of rows 8wv..8wv+7; lane l's chunk is row 8wv + (64n+l)/72, stored
-  // chunk (64n+l)%72, fetched from that row's chunk chunk_swz(., row). The
-  // row is one of two known to the instruction: 64n/72, or the next from lane
-  // 72(64n/72 + 1) - 64n on. goff[n] holds the chunk's byte offset in its
-  // row, less the 1024 (n % 4) that the copy's instruction offset adds back
-  // (plus 3072 on the 32-bit path, whose base sits 3072 bytes below the cache
-  // so that every offset stays non-negative).
-  constexpr uint32_t kBias = kOff32 ? 3072u : 0u;
-  uint32_t goff[kGatherInsts];
-#pragma unroll
-  for (int n = 0; n < kGatherInsts; ++n) {
-    const int qc = 64 * n + lane;
-    const int rl = qc / 72, lc = qc % 72;
-    goff[n] = (uint32_t)(16 * chunk_swz(lc, 8 * wv + rl)) + kBias - 1024u * (n % 4);
-  }
-  const uint8_t *kv_base = kv - kBias;
+  const TileGather<kOff32> tg(kv, lds_tiles, wv, lane);
   // row ids of this wave's eight rows of a tile (read one tile ahead of the
   // copy that needs them, so the copy never waits on this LDS read)
   auto rowids = [&](int tile, u32x4_t &ra, u32x4_t &rb) {
@@ -340,58 +531,10 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     rb = *reinterpret_cast<const u32x4_t *>(s_rowid + tile * kTileN + 8 * wv + 4);
   };
   auto gather = [&](int tile, const u32x4_t ra, const u32x4_t rb) {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(
-        lds_tiles + (uint32_t)(tile & (kStages - 1)) * kTileBytes + 8 * wv * kRowBytes);
-    const uint32_t rid[8] = {ra.x & ~kInvalid, ra.y & ~kInvalid, ra.z & ~kInvalid, ra.w & ~kInvalid,
-                             rb.x & ~kInvalid, rb.y & ~kInvalid, rb.z & ~kInvalid, rb.w & ~kInvalid};
-    if constexpr (kOff32) {
-      uint32_t v[kGatherInsts];
-#pragma unroll
-      for (int n = 0; n < kGatherInsts; ++n) {
-        const int q0 = (64 * n) / 72;
-        const int split_lane = 72 * (q0 + 1) - 64 * n;
-        const uint32_t r = (q0 == 7 || lane < split_lane) ? rid[q0] : rid[q0 + 1];
-        v[n] = __umul24(r, (uint32_t)kRowBytes) + goff[n];
-      }
-      lds_copy9(kv_base, v, lds);
-    } else {
-      uint64_t v[kGatherInsts];
-#pragma unroll
-      for (int n = 0; n < kGatherInsts; ++n) {
-        const int q0 = (64 * n) / 72;
-        const int split_lane = 72 * (q0 + 1) - 64 * n;
-        const uint32_t r = (q0 == 7 || lane < split_lane) ? rid[q0] : rid[q0 + 1];
-        v[n] = (uint64_t)((int64_t)(uintptr_t)kv + (int64_t)r * kRowBytes + (int32_t)goff[n]);
-      }
-      lds_copy9(v, lds);
-    }
+    tg.copy(tile & (kStages - 1), ra, rb);
   };
 
-  // Operand offsets inside a tile (loop-invariant). Logits A operand: lane
-  // (g, i) reads tile row tile_row(m, i), chunk 4s + g; M-tile 1 is 16 rows
-  // further with the same permutation. Latent steps s use a_lat[s & 3] plus
-  // 256 (s >> 2); the two RoPE steps use a_rope[s - 16].
-  const int ar = tile_row(0, j);
-  uint32_t a_lat[4], a_rope[2];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) a_lat[s] = ar * kRowBytes + 16 * chunk_swz(4 * s + g, ar);
-#pragma unroll
-  for (int s = 0; s < 2; ++s) a_rope[s] = ar * kRowBytes + 16 * chunk_swz(64 + 4 * s + g, ar);
-  // Value operand: lane (g, j), e = j / 4: transposed read L covers rows
-  // tile_row(L, 4g + e), dims 4(j & 3) .. +4 of the 16-dim tile nt. Tile nt
-  // uses v_off[nt & 7] plus 256 (nt >> 3); read L = 1 is 16 rows further.
-  const int vr = tile_row(0, 4 * g + (j >> 2));
-  uint32_t v_off[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c)
-    v_off[c] = vr * kRowBytes + 16 * ((2 * c + ((j & 3) >> 1)) ^ (vr & 15)) + 8 * (j & 1);
-  // Rows of this lane's 8 logits: value (m, r) is tile row tile_row(m, 4g + r).
-  int lrow[2][4];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) lrow[m][r] = tile_row(m, 4 * g + r);
-
+  const TileLane tl = tile_lane(g, j);
   f32x4_t o[32];
 #pragma unroll
   for (int nt = 0; nt < 32; ++nt) o[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -429,116 +572,8 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
 
     // (a fully masked tile is computed like any other: its logits are all
     // -inf and add nothing)
-    const uint32_t vmask = s_vmask[tile];
-    const lds_u8 *tb = tiles + (tile & (kStages - 1)) * kTileBytes;
-
-    // logits (transposed): acc[m][r] = S[head 16wv + j][row lrow[m][r]], A
-    // operands read one k-step ahead of the MFMAs
-    f32x4_t acc[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
-    auto a_off = [&](int s_) -> uint32_t {
-      return s_ < 16 ? a_lat[s_ & 3] + 256 * (s_ >> 2) : a_rope[s_ - 16];
-    };
-    // A operands run kAhead k-steps ahead of their MFMAs
-    constexpr int kAhead = 4;
-    u32x4_t abuf[kSteps][2];
-#pragma unroll
-    for (int s_ = 0; s_ < kAhead; ++s_)
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-        abuf[s_][m] = *(const __attribute__((address_space(3))) u32x4_t *)(tb + a_off(s_) + m * 16 * kRowBytes);
-#pragma unroll
-    for (int s_ = 0; s_ < kSteps; ++s_) {
-      if (s_ + kAhead < kSteps) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-          abuf[s_ + kAhead][m] = *(const __attribute__((address_space(3))) u32x4_t *)(
-              tb + a_off(s_ + kAhead) + m * 16 * kRowBytes);
-      }
-#pragma unroll
-      for (int m = 0; m < 2; ++m) acc[m] = mfma_16x16x32_bf16(abuf[s_][m], qf[s_], acc[m]);
-    }
-    // issue order: 2 * kAhead operand reads, then one read per MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * (kSteps - kAhead); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
-
-    // Value operands (transposed reads, two per 16-dim tile nt) run kVAhead
-    // tiles ahead of their MFMAs; the first kVAhead go out before the softmax
-    // so their latency hides under it.
-    auto vread = [&](int nt) -> u32x4_t {
-      const lds_u8 *vp = tb + v_off[nt & 7] + 256 * (nt >> 3);
-      const uint2 v0 = lds_read_tr16(vp);
-      const uint2 v1 = lds_read_tr16(vp + 16 * kRowBytes);
-      return u32x4_t{v0.x, v0.y, v1.x, v1.y};
-    };
-    constexpr int kVAhead = 6;
-    u32x4_t vbuf[32];
-#pragma unroll
-    for (int nt = 0; nt < kVAhead; ++nt) vbuf[nt] = vread(nt);
-    __builtin_amdgcn_sched_barrier(0);
-    if (vmask != 0xFFFFFFFFu) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (!((vmask >> lrow[m][r]) & 1u)) acc[m][r] = -INFINITY;
-    }
-    // softmax of head 16wv + j in base 2 against a reference maximum m_run
-    // fixed by the head's first valid tile: p = 2^(x - m_run). A later tile
-    // may exceed it by up to kHeadroom (p <= 2^kHeadroom keeps every sum
-    // finite); beyond that the whole split restarts with a higher reference,
-    // so the accumulated output is never rescaled in the loop.
-    float mx = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
-                     fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
-    mx = group4_max(mx) * scale_log2;
-    m_run = m_run == -INFINITY ? mx : m_run;
-    const bool over = mx > m_run + kHeadroom;
-    m_run = over ? mx : m_run;  // per lane: a restarted pass starts from here
-    overflow |= over;
-    // every lane writes the same word, so no branch splits the tile's code;
-    // the flag is read by all waves after the next barrier (a restarted
-    // split discards whatever this tile accumulates)
-    s_over[wv] = __ballot(overflow) != 0ull ? 1 : 0;
-    // until the head's first valid row every logit is -inf: subtract 0, not -inf
-    const float m_sub = m_run == -INFINITY ? 0.0f : m_run;
-    float p[2][4];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[m][r] = fast_exp2(fmaf(acc[m][r], scale_log2, -m_sub));
-        l_run += p[m][r];
-      }
-    // P as the A operand of PV: head j, k-slots 8g + 4m + r <-> rows lrow[m][r].
-    // p = hi + lo in bf16 to 2^-16 relative: bf16 rounding of p alone (2^-9)
-    // is too coarse for rows that attend to only a few positions.
-    u32x4_t pa, pl;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t hi = pack_bf16x2(p[m][2 * h], p[m][2 * h + 1]);
-        const float r0 = p[m][2 * h] - __uint_as_float(hi << 16);
-        const float r1 = p[m][2 * h + 1] - __uint_as_float(hi & 0xFFFF0000u);
-        pa[2 * m + h] = hi;
-        pl[2 * m + h] = pack_bf16x2(r0, r1);
-      }
-    // PV in a fixed order: each pair of MFMAs is preceded by the reads of
-    // the tile kVAhead further on. (Left to itself the scheduler sinks every
-    // read to just before its MFMAs, which exposes the whole LDS latency once
-    // per pair.)
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int nt = 0; nt < 32; ++nt) {
-      if (nt + kVAhead < 32) vbuf[nt + kVAhead] = vread(nt + kVAhead);
-      o[nt] = mfma_16x16x32_bf16(pa, vbuf[nt], o[nt]);
-      o[nt] = mfma_16x16x32_bf16(pl, vbuf[nt], o[nt]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    mla_tile(tiles + (tile & (kStages - 1)) * kTileBytes, s_vmask[tile], tl, qf, o, m_run, l_run,
+             overflow, scale_log2, s_over + wv);
   };
 
   // Passes over the split: normally one. A pass in which some tile
@@ -748,6 +783,335 @@ __global__ __launch_bounds__(256) void sparse_mla_generic_kernel(
   if (lse != nullptr && tid == 0) lse[rh] = l_run > 0.0f ? m_run * kLn2 + logf(l_run) : -INFINITY;
 }
 
+
+// ---------------------------------------------------------------------------
+// Query-blocked sparse MLA ("Making GLM-5.2 Sparse on TPUs", section "Reuse
+// pages across queries": a block of queries loads the union of its selected
+// rows once and restores each query's own support with a membership mask
+// before the softmax; the union is sorted and compacted, and membership is
+// indexed by compact union slot).
+//
+// A workgroup serves 64 columns (query, head) of one block of QB consecutive
+// query rows: QB = 4 queries x 16 heads when a query has 16 or more heads
+// (one workgroup per group of 16 heads), QB = 8 queries x 8 heads for
+// 8-head shards. Every row tile of the union feeds all 64 columns, as a tile
+// of one query's rows feeds its 64 heads in the unblocked kernel; so the
+// blocked form pays where a query alone has fewer than 64 heads to offer a
+// tile, and saves row loads wherever the block's selections overlap.
+// ---------------------------------------------------------------------------
+
+constexpr int kQbMaxCands = 16384;  // QB * k of one block: the union kernel's LDS lists
+constexpr int kUnionThreads = 256;
+constexpr int kChunkRows = kMaxRowsPerSplit;  // union slots per row table of the attention kernel
+
+// Physical row of position pos of sequence b (the page id clamped into the pool).
+__device__ __forceinline__ uint32_t phys_row(const int32_t *block_table, int64_t bt_stride, int b,
+                                             uint32_t pos, int page_size, FastDiv pdiv,
+                                             int64_t num_pages) {
+  const uint32_t pidx = fast_div(pos, pdiv);
+  const int64_t page = clamp_page(block_table[(int64_t)b * bt_stride + pidx], num_pages);
+  return (uint32_t)(page * page_size + (pos - pidx * (uint32_t)page_size));
+}
+
+// One workgroup per block m (rows QB m .. QB m + QB - 1): the union of the
+// rows' selected positions as physical rows, ascending by position, with a
+// QB-bit membership mask per slot (bit q: row QB m + q selected it); slots
+// beyond u_count[m] are unused. Keys are (position << 3 | q), entries outside
+// [0, t] are dropped. The rows' lists are merged pairwise (merge path: an
+// element's slot is its index plus the number of smaller keys in the partner
+// list, found by binary search), then runs of one position are compacted
+// into one slot. This needs every row's valid entries first and strictly
+// ascending (what dsa_topk and dsa_page_topk write) and the rows in one
+// sequence; any other block takes its rows' entries as they are, one slot and
+// one membership bit each (a position listed twice then counts twice, as in
+// the unblocked kernel).
+template <int QB>
+__global__ __launch_bounds__(kUnionThreads) void mla_union_kernel(
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ cu_q, int batch, int total_q, int max_seq_len, int64_t bt_stride,
+    int page_size, FastDiv pdiv, int64_t num_pages, const int32_t *__restrict__ indices, int k,
+    FastDiv kdiv, uint32_t *__restrict__ u_rows, uint8_t *__restrict__ u_mask,
+    int32_t *__restrict__ u_count) {
+  constexpr uint32_t kSent = 0xFFFFFFFFu;
+  constexpr int kW = kUnionThreads / kWave;
+  __shared__ uint32_t s_a[kQbMaxCands];
+  __shared__ uint32_t s_b[kQbMaxCands];
+  __shared__ int s_bq[QB], s_tq[QB], s_nq[QB];
+  __shared__ int s_bad;
+  __shared__ uint32_t s_wsum[kW];
+  const int m = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int cap = QB * k;
+  const int64_t ubase = (int64_t)m * cap;
+  if (tid < QB) s_nq[tid] = 0;
+  if (tid == 0) s_bad = 0;
+  // the rows' sequences and positions (a wave per row)
+  for (int q = wv; q < QB; q += kW) {
+    const int r = m * QB + q;
+    RowInfo ri{0, -1};
+    if (r < total_q) ri = row_info(cu_q, seq_lens, batch, total_q, max_seq_len, r);
+    if (lane == 0) {
+      s_bq[q] = ri.b;
+      s_tq[q] = ri.t;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < cap; e += kUnionThreads) {
+    const int q = (int)fast_div((uint32_t)e, kdiv);
+    const int r = m * QB + q;
+    const int pos = r < total_q ? indices[(int64_t)r * k + (e - q * k)] : -1;
+    const bool valid = pos >= 0 && pos <= s_tq[q];
+    s_a[e] = valid ? ((uint32_t)pos << 3) | (uint32_t)q : kSent;
+    if (valid) atomicAdd(&s_nq[q], 1);
+  }
+  __syncthreads();
+  // canonical lists: in each row the valid entries come first, strictly ascending
+  for (int e = tid; e < cap; e += kUnionThreads) {
+    const int q = (int)fast_div((uint32_t)e, kdiv);
+    if (e + 1 < (q + 1) * k) {
+      const uint32_t x = s_a[e], y = s_a[e + 1];
+      if (y != kSent && (x == kSent || (x >> 3) >= (y >> 3))) s_bad = 1;
+    }
+  }
+  bool one_seq = true;
+#pragma unroll
+  for (int q = 1; q < QB; ++q)
+    if (m * QB + q < total_q && s_bq[q] != s_bq[0]) one_seq = false;
+  __syncthreads();
+  if (s_bad != 0 || !one_seq) {
+    // unused slots read a stand-in row that holds written data: position 0
+    // of the first row's sequence that has a valid entry (no such row: an
+    // empty union)
+    int qs = -1;
+#pragma unroll
+    for (int q = QB - 1; q >= 0; --q)
+      if (s_nq[q] > 0) qs = q;
+    if (qs < 0) {
+      if (tid == 0) u_count[m] = 0;
+      return;
+    }
+    const uint32_t safe = phys_row(block_table, bt_stride, s_bq[qs], 0u, page_size, pdiv, num_pages);
+    for (int e = tid; e < cap; e += kUnionThreads) {
+      const int q = (int)fast_div((uint32_t)e, kdiv);
+      const uint32_t x = s_a[e];
+      const bool valid = x != kSent;
+      u_rows[ubase + e] = valid ? phys_row(block_table, bt_stride, s_bq[q], x >> 3, page_size, pdiv,
+                                           num_pages)
+                                : safe;
+      u_mask[ubase + e] = valid ? (uint8_t)(1u << q) : (uint8_t)0;
+    }
+    if (tid == 0) u_count[m] = cap;
+    return;
+  }
+  // merge rounds: lists of w rows at offsets p k (p a multiple of w), merged
+  // in pairs into lists of 2w rows at the left one's offset
+  uint32_t *src = s_a, *dst = s_b;
+  auto list_len = [&](int p, int w) {
+    int n = 0;
+    for (int q = p; q < p + w; ++q) n += s_nq[q];
+    return n;
+  };
+#pragma unroll
+  for (int w = 1; w < QB; w *= 2) {
+    for (int e = tid; e < cap; e += kUnionThreads) {
+      const int q = (int)fast_div((uint32_t)e, kdiv);
+      const int lst = q / w;
+      const int p = (lst & ~1) * w;  // first row of the pair's left list
+      const bool left = (lst & 1) == 0;
+      const int loff = p * k, roff = (p + w) * k;
+      const int nl = list_len(p, w), nr = list_len(p + w, w);
+      const int i = e - (left ? loff : roff);
+      if (i >= (left ? nl : nr)) continue;
+      const uint32_t x = src[e];
+      const uint32_t *po = src + (left ? roff : loff);
+      int lo = 0, hi = left ? nr : nl;  // keys below x in the partner list
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (po[mid] < x) lo = mid + 1;
+        else hi = mid;
+      }
+      dst[loff + i + lo] = x;
+    }
+    __syncthreads();
+    uint32_t *t = src;
+    src = dst;
+    dst = t;
+  }
+  // compaction: each thread takes a contiguous range of the merged list, and
+  // the run starts (new positions) get consecutive slots in order
+  const int N = list_len(0, QB);
+  const int per = (N + kUnionThreads - 1) / kUnionThreads;
+  const int e0 = min(N, tid * per), e1 = min(N, e0 + per);
+  uint32_t cnt = 0;
+  for (int e = e0; e < e1; ++e) cnt += (e == 0 || (src[e] >> 3) != (src[e - 1] >> 3)) ? 1u : 0u;
+  const uint32_t incl = wave_prefix_sum(cnt);
+  if (lane == kWave - 1) s_wsum[wv] = incl;
+  __syncthreads();
+  uint32_t slot = incl - cnt, total = 0;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    slot += w < wv ? s_wsum[w] : 0u;
+    total += s_wsum[w];
+  }
+  for (int e = e0; e < e1; ++e) {
+    const uint32_t pos = src[e] >> 3;
+    if (e > 0 && (src[e - 1] >> 3) == pos) continue;
+    uint32_t mk = 0;
+    for (int e2 = e; e2 < N && (src[e2] >> 3) == pos; ++e2) mk |= 1u << (src[e2] & 7u);
+    u_rows[ubase + slot] = phys_row(block_table, bt_stride, s_bq[0], pos, page_size, pdiv, num_pages);
+    u_mask[ubase + slot] = (uint8_t)mk;
+    ++slot;
+  }
+  if (tid == 0) u_count[m] = (int32_t)total;
+}
+
+// Attention over a block's union: one workgroup per (block, group of 64 / QB
+// heads), the four waves over the 64 columns (wave w: columns 16w..16w+15,
+// column c = query c / (64 / QB) of the block, head c % (64 / QB) of the
+// group). The union is walked in chunks of kChunkRows slots (row table and
+// per-query tile masks in LDS), each chunk's tiles through the same four-stage
+// ring and tile compute as the unblocked kernel, with each lane's row mask that
+// of its column's query. The whole union stays in one workgroup, so there are
+// no split partials.
+template <bool kOff32, int QB>
+__global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_qblock_kernel(
+    int total_q, int n_heads, int n_hg, const uint16_t *__restrict__ q,
+    const uint8_t *__restrict__ kv, const uint32_t *__restrict__ u_rows,
+    const uint8_t *__restrict__ u_mask, const int32_t *__restrict__ u_count, int cap,
+    float scale_log2, float *__restrict__ out, float *__restrict__ lse) {
+  constexpr int kHg = kH / QB;  // heads of a query in this workgroup
+  __shared__ __attribute__((aligned(1024))) uint8_t s_tiles[kStages * kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t s_rowid[kChunkRows + kTileN];
+  __shared__ uint32_t s_vm[kChunkRows / kTileN + 1][QB];
+  __shared__ float s_ml[kH][2];
+  __shared__ int s_over[kMlaWaves];
+
+  // the n_hg workgroups of a block are numbered onto one XCD (block ids are
+  // dealt to the 8 XCDs in turn), so they read the union's rows from its L2
+  const int bid = (int)blockIdx.x;
+  const int xcd = bid % kXcds, rest = bid / kXcds;
+  const int hgi = rest % n_hg;
+  const int m = (rest / n_hg) * kXcds + xcd;
+  const int n_blocks = (total_q + QB - 1) / QB;
+  if (m >= n_blocks) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  const int64_t ubase = (int64_t)m * cap;
+  const int count = min(max(u_count[m], 0), cap);
+
+  // this lane's column: query qi of the block (row m QB + qi), head `head`
+  const int col = 16 * wv + j;
+  const int qi = col / kHg;
+  const int head = hgi * kHg + col % kHg;
+  const int qrow = min(m * QB + qi, total_q - 1);
+  u32x4_t qf[kSteps];
+  const uint16_t *qp = q + ((int64_t)qrow * n_heads + head) * kD + 8 * g;
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) qf[s] = ldg16(qp + 32 * s);
+
+  const lds_u8 *tiles = (const lds_u8 *)s_tiles;
+  const TileGather<kOff32> tg(kv, (uint32_t)(uintptr_t)tiles, wv, lane);
+  const TileLane tl = tile_lane(g, j);
+  f32x4_t o[32];
+#pragma unroll
+  for (int nt = 0; nt < 32; ++nt) o[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY, l_run = 0.0f;
+  bool overflow = false;
+  if (tid < kMlaWaves) s_over[tid] = 0;
+
+  u32x4_t ra_n, rb_n;
+  auto rowids = [&](int tile, u32x4_t &ra, u32x4_t &rb) {
+    ra = *reinterpret_cast<const u32x4_t *>(s_rowid + tile * kTileN + 8 * wv);
+    rb = *reinterpret_cast<const u32x4_t *>(s_rowid + tile * kTileN + 8 * wv + 4);
+  };
+  // one chunk of the union: row table, then its tiles through the ring
+  auto chunk = [&](int c0) {
+    const int n = min(kChunkRows, count - c0);
+    const int ntiles = (n + kTileN - 1) / kTileN;
+    // slots past the union repeat slot c0's row (a valid stand-in) with no
+    // membership; every lane loads (indices inside the chunk), no branch
+    for (int e0 = 0; e0 < ntiles * kTileN; e0 += kMlaThreads) {
+      const int e = e0 + tid;
+      const bool in = e < n;
+      const int64_t src = ubase + c0 + (in ? e : 0);
+      const uint32_t rid = u_rows[src];
+      const uint32_t mk = in ? u_mask[src] : 0u;
+      if (e < ntiles * kTileN) s_rowid[e] = rid;
+#pragma unroll
+      for (int qq = 0; qq < QB; ++qq) {
+        const uint64_t bits = __ballot(((mk >> qq) & 1u) != 0u && e < ntiles * kTileN);
+        if (lane == 0 && e < ntiles * kTileN) {
+          s_vm[e / kTileN][qq] = (uint32_t)bits;
+          if (e + kTileN < ntiles * kTileN) s_vm[e / kTileN + 1][qq] = (uint32_t)(bits >> 32);
+        }
+      }
+    }
+    // (the compiler's loads have landed before the first direct copies)
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __syncthreads();
+    for (int tile = 0; tile < min(ntiles, kStages - 1); ++tile) {
+      rowids(tile, ra_n, rb_n);
+      tg.copy(tile & (kStages - 1), ra_n, rb_n);
+    }
+    rowids(max(min(kStages - 1, ntiles - 1), 0), ra_n, rb_n);
+    for (int tile = 0; tile < ntiles; ++tile) {
+      const int ahead = min(ntiles - 1 - tile, kStages - 2);
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0070 | ((2 * kGatherInsts) & 15) | (((2 * kGatherInsts) >> 4) << 14));
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0070 | (kGatherInsts & 15) | ((kGatherInsts >> 4) << 14));
+      else __builtin_amdgcn_s_waitcnt(0x0070);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      if (tile + kStages - 1 < ntiles) tg.copy((tile + kStages - 1) & (kStages - 1), ra_n, rb_n);
+      rowids(min(tile + kStages, ntiles - 1), ra_n, rb_n);
+      mla_tile(tiles + (tile & (kStages - 1)) * kTileBytes, s_vm[tile][qi], tl, qf, o, m_run, l_run,
+               overflow, scale_log2, s_over + wv);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no direct load of this chunk in flight
+    __syncthreads();                     // stages and row table free for the next chunk
+  };
+  // passes over the union (a pass that overflowed the headroom is walked again
+  // from the raised references, as in the unblocked kernel)
+  for (;;) {
+    for (int c0 = 0; c0 < count; c0 += kChunkRows) chunk(c0);
+    __syncthreads();
+    if ((s_over[0] | s_over[1] | s_over[2] | s_over[3]) == 0) break;
+    __syncthreads();
+    if (tid < kMlaWaves) s_over[tid] = 0;
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) o[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    l_run = 0.0f;
+    overflow = false;
+    __syncthreads();
+  }
+
+  const float l_tot = group4_sum(l_run);
+  if (g == 0) {
+    s_ml[col][0] = m_run;
+    s_ml[col][1] = l_tot;
+  }
+  __syncthreads();
+  // o[nt][r] of lane (g, j): column 16 wv + 4 g + r, dim 16 nt + j
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int c = 16 * wv + 4 * g + r;
+    const int row_c = m * QB + c / kHg;
+    if (row_c >= total_q) continue;
+    const float l = s_ml[c][1];
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    float *op = out + ((int64_t)row_c * n_heads + hgi * kHg + c % kHg) * kDL + j;
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) op[16 * nt] = o[nt][r] * inv;
+  }
+  if (lse != nullptr && tid < kH) {
+    const int row_c = m * QB + tid / kHg;
+    if (row_c < total_q) {
+      const float mm = s_ml[tid][0], l = s_ml[tid][1];
+      lse[(int64_t)row_c * n_heads + hgi * kHg + tid % kHg] =
+          l > 0.0f ? mm * kLn2 + logf(l) : -INFINITY;
+    }
+  }
+}
+
 bool mfma_shape(int32_t q_dtype, int32_t n_heads, int32_t d_latent, int32_t d_rope) {
   return q_dtype == DSA_BF16 && n_heads == kH && d_latent == kDL && d_rope == kDR;
 }
@@ -861,6 +1225,77 @@ hipError_t launch_sparse_mla(const BatchArgs &bt, const MlaLayer *ly, int n_laye
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// query-blocked launcher
+// ---------------------------------------------------------------------------
+
+int mla_qblock_qb(int32_t n_heads) { return n_heads >= 16 ? 4 : 8; }
+
+bool mla_qblock_supported(int32_t q_dtype, int32_t n_heads, int32_t d_latent, int32_t d_rope,
+                          int32_t k) {
+  if (q_dtype != DSA_BF16 || d_latent != kDL || d_rope != kDR) return false;
+  if (!(n_heads == 8 || (n_heads >= 16 && n_heads <= kH && n_heads % 16 == 0))) return false;
+  return (int64_t)mla_qblock_qb(n_heads) * k <= kQbMaxCands;
+}
+
+namespace {
+struct QbLayout {
+  int64_t n_blocks, cap;
+  size_t rows_off, mask_off, count_off, bytes;
+};
+QbLayout qb_layout(int32_t total_q, int32_t n_heads, int32_t k) {
+  QbLayout L{};
+  const int QB = mla_qblock_qb(n_heads);
+  L.n_blocks = (total_q + QB - 1) / QB;
+  L.cap = (int64_t)QB * k;
+  auto up16 = [](size_t x) { return (x + 15) & ~(size_t)15; };
+  L.rows_off = 0;
+  L.mask_off = up16((size_t)L.n_blocks * L.cap * sizeof(uint32_t));
+  L.count_off = L.mask_off + up16((size_t)L.n_blocks * L.cap);
+  L.bytes = L.count_off + up16((size_t)L.n_blocks * sizeof(int32_t));
+  return L;
+}
+}  // namespace
+
+size_t mla_qblock_workspace_bytes(int32_t total_q, int32_t n_heads, int32_t k) {
+  if (total_q < 1 || n_heads < 1 || k < 1) return 0;
+  return qb_layout(total_q, n_heads, k).bytes;
+}
+
+hipError_t launch_sparse_mla_qblocked(const BatchArgs &bt, const MlaLayer &ly, int32_t n_heads,
+                                      const int32_t *indices, int32_t k, float scale,
+                                      void *workspace, hipStream_t stream) {
+  if (bt.total_q == 0) return hipSuccess;
+  const int QB = mla_qblock_qb(n_heads);
+  const QbLayout L = qb_layout(bt.total_q, n_heads, k);
+  if (L.n_blocks > 0x7FFFFFFF / kXcds) return hipErrorInvalidConfiguration;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  uint32_t *u_rows = reinterpret_cast<uint32_t *>(ws + L.rows_off);
+  uint8_t *u_mask = ws + L.mask_off;
+  int32_t *u_count = reinterpret_cast<int32_t *>(ws + L.count_off);
+  const CacheArgs &kv = ly.kv;
+  const FastDiv pdiv = make_fast_div((uint32_t)kv.page_size);
+  const FastDiv kdiv = make_fast_div((uint32_t)k);
+  auto uk = QB == 4 ? mla_union_kernel<4> : mla_union_kernel<8>;
+  hipLaunchKernelGGL(uk, dim3((unsigned)L.n_blocks), dim3(kUnionThreads), 0, stream, bt.block_table,
+                     bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, bt.bt_stride,
+                     kv.page_size, pdiv, kv.num_pages, indices, k, kdiv, u_rows, u_mask, u_count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_hg = n_heads / (kH / QB);
+  const int64_t blocks = (L.n_blocks + kXcds - 1) / kXcds * kXcds * n_hg;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const uint64_t pool_bytes = (uint64_t)kv.num_pages * (uint64_t)kv.page_size * kRowBytes;
+  const bool off32 = pool_bytes + 4096 <= (1ull << 32);
+  auto ak = QB == 4 ? (off32 ? sparse_mla_qblock_kernel<true, 4> : sparse_mla_qblock_kernel<false, 4>)
+                    : (off32 ? sparse_mla_qblock_kernel<true, 8> : sparse_mla_qblock_kernel<false, 8>);
+  hipLaunchKernelGGL(ak, dim3((unsigned)blocks), dim3(kMlaThreads), 0, stream, bt.total_q, n_heads,
+                     n_hg, static_cast<const uint16_t *>(ly.q),
+                     static_cast<const uint8_t *>(kv.data), u_rows, u_mask, u_count, (int)L.cap,
+                     scale * kLog2e, ly.out, ly.lse);
+  return hipGetLastError();
 }
 
 }  // namespace dsa

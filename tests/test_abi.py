@@ -183,6 +183,41 @@ def test_mla_noalloc_limit_covers_every_decode_batch_at_k2048():
     assert L.lib.dsa_sparse_mla_workspace_size(32, 64, 512, 65536) > L.DSA_MLA_NOALLOC_SCRATCH_BYTES
 
 
+def _mla_qb(b=None, q=FAKE, qd=L.DSA_BF16, H=64, DL=512, DR=64, c=None, idx=FAKE, k=2048,
+            scale=0.0625, out=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 40):
+    b = _batch() if b is None else b
+    c = _cache(row_elems=576) if c is None else c
+    return L.lib.dsa_sparse_mla_fwd_qblocked(ctypes.byref(b) if b is not False else None, q, qd, H,
+                                             DL, DR, ctypes.byref(c) if c is not False else None,
+                                             idx, k, scale, out, lse, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=False), 1), (dict(q=None), 1), (dict(idx=None), 1), (dict(out=None), 1),
+    (dict(c=False), 1), (dict(k=0), 2), (dict(scale=0.0), 2), (dict(scale=float("nan")), 2),
+    (dict(out=FAKE + 4), 2), (dict(DR=32), 2), (dict(qd=L.DSA_F32), 3),
+    (dict(ws=None), 4), (dict(wsb=16), 4), (dict(ws=FAKE + 8), 4),
+    # head counts other than 8 or a multiple of 16 up to 64, other row widths,
+    # or unions over 16384 slots (QB k) are not supported
+    (dict(H=12), 5), (dict(H=128), 5), (dict(H=4), 5), (dict(k=4097), 5),
+    (dict(qd=L.DSA_F32, c=_cache(row_elems=576, dtype=L.DSA_F32)), 5),
+    (dict(b=_batch(max_seq_len=1 << 29, bt_stride=(1 << 29) // 64)), 5),
+])
+def test_mla_qblocked_rejects_bad_arguments(kw, code):
+    assert _mla_qb(**kw) == code
+
+
+def test_mla_qblocked_workspace_is_one_union_per_block():
+    # 4-query blocks (16..64 heads) or 8-query blocks (8 heads): per block
+    # QB k row ids (4 B) and masks (1 B, rounded to 16), plus a count per block
+    w64 = L.lib.dsa_sparse_mla_qblocked_workspace_size(4096, 64, 2048)
+    w8 = L.lib.dsa_sparse_mla_qblocked_workspace_size(4096, 8, 2048)
+    assert w64 >= 1024 * 4 * 2048 * 5 and w64 < 1024 * 4 * 2048 * 5 + (1 << 16)
+    assert w8 >= 512 * 8 * 2048 * 5 and w8 < 512 * 8 * 2048 * 5 + (1 << 16)
+    assert L.lib.dsa_sparse_mla_qblocked_workspace_size(0, 64, 2048) == 0
+    assert L.lib.dsa_sparse_mla_qblocked_workspace_size(4097, 64, 2048) > w64
+
+
 def test_workspace_sizes_are_pure_functions_of_bounds():
     assert L.lib.dsa_topk_workspace_size(32, 8192, 2048) == 0
     # rows over 32K: keys and positions of k survivors per chunk (16K positions,

@@ -16,4 +16,5 @@ from .gen import (  # noqa: F401
     raw_numpy,
     PagedRows,
     to_device,
+    locality_indices,
 )

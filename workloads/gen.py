@@ -358,3 +358,41 @@ def to_device(inp: Inputs, device) -> Inputs:
         block_table=mv(inp.block_table), q_idx=mv(inp.q_idx), w=mv(inp.w),
         k_cache=mv(inp.k_cache), k_scale=mv(inp.k_scale),
         q_mla=[mv(q) for q in inp.q_mla], kv_cache=[mv(c) for c in inp.kv_cache])
+
+
+# --------------------------------------------------------------------------
+# selection shapes for attention-only runs (indices drawn, not computed)
+# --------------------------------------------------------------------------
+
+
+def locality_indices(seq_lens, q_lens, k: int, page_size: int, block: int, hot_pages: int,
+                     seed: int) -> torch.Tensor:
+    """Locality-shaped selections: int32 [T, k] index lists in the layout the top-k
+    writes (valid positions ascending, then -1).
+
+    The query rows of each sequence are taken in blocks of ``block`` consecutive
+    rows; a block draws ``hot_pages`` distinct logical pages among those its first
+    row can see, and each of its rows draws min(k, n) distinct positions among the
+    n positions of those pages it can see (position <= its own). Neighbouring
+    queries thus select overlapping rows, the shape in which loading a block's
+    union once pays. Uniform-random selections are the other shape (the top-k of
+    random scores)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    T = sum(q_lens)
+    out = torch.full((T, k), -1, dtype=torch.int32)
+    r = 0
+    for L, q in zip(seq_lens, q_lens):
+        for i0 in range(0, q, block):
+            t0 = L - q + i0
+            n_pages = t0 // page_size + 1
+            pages = torch.randperm(n_pages, generator=g)[: min(hot_pages, n_pages)]
+            cand = (pages[:, None] * page_size + torch.arange(page_size)[None, :]).reshape(-1)
+            for i in range(i0, min(q, i0 + block)):
+                t = L - q + i
+                legal = cand[cand <= t]
+                pick = legal[torch.randperm(legal.numel(), generator=g)[: min(k, legal.numel())]]
+                sel = torch.sort(pick).values.to(torch.int32)
+                out[r + i, : sel.numel()] = sel
+        r += q
+    return out
