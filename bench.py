@@ -67,6 +67,13 @@ def parse():
                          "instead of the top-k tokens, and attend to their positions")
     ap.add_argument("--commands", nargs="*", default=[],
                     help="with --traffic-summary: the commands that made the runs")
+    ap.add_argument("--mla-routes", choices=["topk", "locality"],
+                    help="no step: time dsa_sparse_mla_fwd and dsa_sparse_mla_fwd_qblocked on "
+                         "the same selections (the library's top-k of the workload's scores, "
+                         "or locality-shaped lists) and print one JSON line comparing them")
+    ap.add_argument("--mla-heads", type=int, default=0,
+                    help="with --mla-routes: MLA heads per query (a head-sharded share of the "
+                         "workload's 64), default the workload's")
     return ap.parse_args()
 
 
@@ -351,6 +358,122 @@ def time_kv_append(dsa, inp, wl, kvs, keys, stream, flush, args, reps=10):
 
 
 # --------------------------------------------------------------------------
+# per-query vs query-blocked sparse MLA on one set of selections
+# --------------------------------------------------------------------------
+
+# Locality-shaped selections: a block of 64 consecutive queries draws its rows
+# from a shared set of pages whose size is 2.16 times one query's selection,
+# the union-to-selection ratio of the pages' own example ("Making GLM-5.2
+# Sparse on TPUs", section "Reuse pages across queries": 64 queries of 32
+# pages each with a union of about 69 pages).
+LOCALITY_BLOCK = 64
+LOCALITY_UNION_RATIO = 2.16
+
+
+def mla_routes(args, dsa, wl, dev):
+    from workloads import locality_indices, make_inputs, small_variant
+
+    if args.mla_heads:
+        wl = small_variant(wl, mla_heads=args.mla_heads)
+    inp = make_inputs(wl, device="cuda")
+    T = inp.total_q
+    batch = dsa.Batch(inp.block_table, inp.seq_lens, inp.cu_q, T, inp.max_seq_len, inp.max_q)
+    stream = torch.cuda.current_stream(dev)
+    if args.mla_routes == "topk":
+        keys = dsa.PagedCache(inp.k_cache, inp.k_scale)
+        scores = dsa.indexer_scores(batch, inp.q_idx, inp.w, keys)
+        indices = dsa.topk(batch, scores, wl.topk)
+        del scores
+        recipe = "the library's top-k of the workload's indexer scores"
+    else:
+        hot = int(round(LOCALITY_UNION_RATIO * wl.topk / wl.page_size))
+        indices = locality_indices(inp.seq_lens_host, inp.q_lens_host, wl.topk, wl.page_size,
+                                   block=LOCALITY_BLOCK, hot_pages=hot, seed=wl.seed).to(dev)
+        recipe = (f"blocks of {LOCALITY_BLOCK} queries drawing from {hot} shared pages "
+                  f"({LOCALITY_UNION_RATIO} x one query's {wl.topk} positions)")
+    torch.cuda.synchronize()
+    # union statistics of the blocks the blocked call forms
+    qb = 8 if wl.mla_heads == 8 else 4
+    a = indices.cpu().numpy()
+    union = sel = 0
+    for m in range(0, T, qb):
+        v = a[m:m + qb]
+        v = v[v >= 0]
+        union += int(np.unique(v).size)
+        sel += int(v.size)
+    n_blocks = (T + qb - 1) // qb
+    kv = dsa.PagedCache(inp.kv_cache[0])
+    q = inp.q_mla[0]
+    out_u = torch.empty((T, wl.mla_heads, wl.d_latent), dtype=torch.float32, device=dev)
+    lse_u = torch.empty((T, wl.mla_heads), dtype=torch.float32, device=dev)
+    out_b, lse_b = torch.empty_like(out_u), torch.empty_like(lse_u)
+    ws_u = torch.empty(max(16, dsa.sparse_mla_workspace_size(T, wl.mla_heads, wl.d_latent,
+                                                             wl.topk)), dtype=torch.uint8,
+                       device=dev)
+    ws_b = torch.empty(max(16, dsa.sparse_mla_qblocked_workspace_size(T, wl.mla_heads, wl.topk)),
+                       dtype=torch.uint8, device=dev)
+    flush = torch.ones(1 << 27, dtype=torch.int64, device=dev)
+
+    def per_query():
+        dsa.sparse_mla_fwd(batch, q, kv, indices, wl.d_latent, wl.scale, out=out_u, lse=lse_u,
+                           workspace=ws_u)
+
+    def blocked():
+        dsa.sparse_mla_fwd_qblocked(batch, q, kv, indices, wl.d_latent, wl.scale, out=out_b,
+                                    lse=lse_b, workspace=ws_b)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        ts = []
+        for _ in range(args.steps):
+            if not args.no_flush:
+                flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    ms_u = timed(per_query)
+    ms_b = timed(blocked)
+    # a head-sharded share against the 64-head kernel of the per-query call, its
+    # queries zero-padded to 64 heads (what that kernel would cost such a share)
+    ms_pad = None
+    if wl.mla_heads < 64 and wl.mla_dtype == "bf16" and wl.d_latent == 512 and wl.d_rope == 64:
+        q64 = torch.zeros((T, 64, q.shape[2]), dtype=q.dtype, device=dev)
+        q64[:, :wl.mla_heads] = q
+        out64 = torch.empty((T, 64, wl.d_latent), dtype=torch.float32, device=dev)
+        lse64 = torch.empty((T, 64), dtype=torch.float32, device=dev)
+        ws64 = torch.empty(max(16, dsa.sparse_mla_workspace_size(T, 64, wl.d_latent, wl.topk)),
+                           dtype=torch.uint8, device=dev)
+
+        def padded():
+            dsa.sparse_mla_fwd(batch, q64, kv, indices, wl.d_latent, wl.scale, out=out64,
+                               lse=lse64, workspace=ws64)
+
+        ms_pad = timed(padded)
+        del q64, out64, lse64, ws64
+    rms = float(out_u.double().pow(2).mean().sqrt())
+    diff = float((out_b - out_u).abs().max())
+    if not diff <= 1e-2 * rms:
+        raise RuntimeError(f"blocked and per-query MLA disagree: {diff} vs rms {rms}")
+    line = {"mode": "mla_routes", "workload": wl.name, "selection": args.mla_routes,
+            "selection_recipe": recipe, "n_queries": T, "mla_heads": wl.mla_heads,
+            "topk": wl.topk, "page_size": wl.page_size, "query_block": qb,
+            "union_rows_per_block": union / n_blocks, "selected_rows_per_block": sel / n_blocks,
+            "row_load_reduction": sel / max(1, union),
+            "per_query_ms": ms_u, "blocked_ms": ms_b, "blocked_speedup": ms_u / ms_b,
+            "per_query_padded_to_64_heads_ms": ms_pad,
+            "blocked_speedup_vs_padded": None if ms_pad is None else ms_pad / ms_b,
+            "max_abs_diff_over_rms": diff / rms, "steps": args.steps, "warmup": args.warmup,
+            "timing": "median of HIP-event-timed calls, each after the 1 GiB cache eviction"}
+    print(json.dumps(line), flush=True)
+
+
+# --------------------------------------------------------------------------
 
 
 def main():
@@ -368,6 +491,9 @@ def main():
 
     dev = torch.device("cuda:0")
     wl = WORKLOADS[args.workload]
+    if args.mla_routes:
+        mla_routes(args, dsa, wl, dev)
+        return
     inp = make_inputs(wl, device="cuda")
     T = inp.total_q
     batch = dsa.Batch(inp.block_table, inp.seq_lens, inp.cu_q, T, inp.max_seq_len, inp.max_q)

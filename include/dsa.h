@@ -302,7 +302,7 @@ dsa_status dsa_sparse_mla_fwd_layers(const dsa_batch *batch, int32_t n_layers,
  *   workspace  device, >= dsa_sparse_mla_qblocked_workspace_size(total_q, n_heads, k)
  *
  * Supported: bf16, d_latent 512, d_rope 64, n_heads 8 or 16, 32, 48, 64, QB * k
- * <= 16384, max_seq_len < 2^29 and fewer than 2^32 rows in the cache;
+ * <= 2^20, max_seq_len < 2^29 and fewer than 2^32 rows in the cache;
  * otherwise DSA_ERR_UNSUPPORTED. Other errors as for dsa_sparse_mla_fwd.
  */
 size_t dsa_sparse_mla_qblocked_workspace_size(int32_t total_q, int32_t n_heads, int32_t k);

@@ -800,8 +800,11 @@ __global__ __launch_bounds__(256) void sparse_mla_generic_kernel(
 // tile, and saves row loads wherever the block's selections overlap.
 // ---------------------------------------------------------------------------
 
-constexpr int kQbMaxCands = 16384;  // QB * k of one block: the union kernel's LDS lists
+constexpr int kQbMaxSlots = 1 << 20;  // QB * k of one block (32-bit slot arithmetic)
 constexpr int kUnionThreads = 256;
+constexpr int kUnionWindow = 32768;  // positions per membership map (one byte each, 32 KB of LDS)
+constexpr int kUnionPages = 2048;    // block-table entries staged per window
+constexpr int kUnionBatch = 8;       // index entries a thread requests at once
 constexpr int kChunkRows = kMaxRowsPerSplit;  // union slots per row table of the attention kernel
 
 // Physical row of position pos of sequence b (the page id clamped into the pool).
@@ -813,18 +816,28 @@ __device__ __forceinline__ uint32_t phys_row(const int32_t *block_table, int64_t
   return (uint32_t)(page * page_size + (pos - pidx * (uint32_t)page_size));
 }
 
+// Bytes of x that are not zero, as their top bits (no carry crosses a byte:
+// (b & 0x7F) + 0x7F <= 0xFE).
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
+  return (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
+}
+
 // One workgroup per block m (rows QB m .. QB m + QB - 1): the union of the
 // rows' selected positions as physical rows, ascending by position, with a
 // QB-bit membership mask per slot (bit q: row QB m + q selected it); slots
-// beyond u_count[m] are unused. Keys are (position << 3 | q), entries outside
-// [0, t] are dropped. The rows' lists are merged pairwise (merge path: an
-// element's slot is its index plus the number of smaller keys in the partner
-// list, found by binary search), then runs of one position are compacted
-// into one slot. This needs every row's valid entries first and strictly
-// ascending (what dsa_topk and dsa_page_topk write) and the rows in one
-// sequence; any other block takes its rows' entries as they are, one slot and
-// one membership bit each (a position listed twice then counts twice, as in
-// the unblocked kernel).
+// beyond u_count[m] are unused. Entries outside [0, t] are dropped. The
+// positions are taken in windows of W = min(kUnionWindow, kUnionPages x page
+// size): each window is a byte map in LDS (byte p: the rows that selected
+// position window + p, set with LDS atomics) beside the window's slice of the
+// block table, and two scans of the map in position order give every
+// non-zero byte its slot (each wave walks its quarter of the map 64 words at
+// a time, so the reads are conflict-free, and a prefix over the waves orders
+// the quarters). This needs the rows in one sequence and every row's valid
+// entries first and strictly ascending (what dsa_topk and dsa_page_topk
+// write), so that a slot stands for one position of one sequence; any other
+// block takes its rows' entries as they are, one slot and one membership bit
+// each (a position listed twice then counts twice, as in the unblocked
+// kernel).
 template <int QB>
 __global__ __launch_bounds__(kUnionThreads) void mla_union_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
@@ -832,10 +845,11 @@ __global__ __launch_bounds__(kUnionThreads) void mla_union_kernel(
     int page_size, FastDiv pdiv, int64_t num_pages, const int32_t *__restrict__ indices, int k,
     FastDiv kdiv, uint32_t *__restrict__ u_rows, uint8_t *__restrict__ u_mask,
     int32_t *__restrict__ u_count) {
-  constexpr uint32_t kSent = 0xFFFFFFFFu;
   constexpr int kW = kUnionThreads / kWave;
-  __shared__ uint32_t s_a[kQbMaxCands];
-  __shared__ uint32_t s_b[kQbMaxCands];
+  constexpr int kWords = kUnionWindow / 4;
+  constexpr int kWaveWords = kWords / kW;
+  __shared__ __attribute__((aligned(16))) uint32_t s_map[kWords];
+  __shared__ uint32_t s_pg[kUnionPages + 2];
   __shared__ int s_bq[QB], s_tq[QB], s_nq[QB];
   __shared__ int s_bad;
   __shared__ uint32_t s_wsum[kW];
@@ -855,28 +869,65 @@ __global__ __launch_bounds__(kUnionThreads) void mla_union_kernel(
       s_tq[q] = ri.t;
     }
   }
+  // the first window's map is cleared before the count pass, which fills it
+  const int W = (int)min((int64_t)kUnionWindow, (int64_t)kUnionPages * page_size);
+  u32x4_t *m4 = reinterpret_cast<u32x4_t *>(s_map);
+  for (int i = tid; i < kWords / 4; i += kUnionThreads) m4[i] = u32x4_t{0u, 0u, 0u, 0u};
   __syncthreads();
-  for (int e = tid; e < cap; e += kUnionThreads) {
-    const int q = (int)fast_div((uint32_t)e, kdiv);
+  // entry e of the block: row q = e / k, slot e - q k of its list (-1 past the batch)
+  auto entry = [&](int e, int &q) -> int {
+    q = (int)fast_div((uint32_t)e, kdiv);
     const int r = m * QB + q;
-    const int pos = r < total_q ? indices[(int64_t)r * k + (e - q * k)] : -1;
-    const bool valid = pos >= 0 && pos <= s_tq[q];
-    s_a[e] = valid ? ((uint32_t)pos << 3) | (uint32_t)q : kSent;
-    if (valid) atomicAdd(&s_nq[q], 1);
-  }
-  __syncthreads();
-  // canonical lists: in each row the valid entries come first, strictly ascending
-  for (int e = tid; e < cap; e += kUnionThreads) {
-    const int q = (int)fast_div((uint32_t)e, kdiv);
-    if (e + 1 < (q + 1) * k) {
-      const uint32_t x = s_a[e], y = s_a[e + 1];
-      if (y != kSent && (x == kSent || (x >> 3) >= (y >> 3))) s_bad = 1;
+    return r < total_q ? indices[(int64_t)r * k + (e - q * k)] : -1;
+  };
+  // window [w0, w0 + W) of the map: every valid entry in it sets its row's bit
+  auto insert = [&](int x, int q, int w0) {
+    if (x >= w0 && x - w0 < W && x <= s_tq[q]) {
+      const int p = x - w0;
+      atomicOr(&s_map[p >> 2], (1u << q) << (8 * (p & 3)));
+    }
+  };
+  // count pass: valid entries per row, whether every row's list is canonical
+  // (valid entries first, strictly ascending), and the first window's map;
+  // each thread requests kUnionBatch entries (and their successors) at once
+  uint32_t nq[QB];
+#pragma unroll
+  for (int q = 0; q < QB; ++q) nq[q] = 0;
+  bool bad = false;
+  for (int e0 = tid; e0 < cap; e0 += kUnionBatch * kUnionThreads) {
+    int xs[kUnionBatch], ys[kUnionBatch], qs[kUnionBatch];
+#pragma unroll
+    for (int j = 0; j < kUnionBatch; ++j) {
+      const int e = e0 + j * kUnionThreads;
+      int q1;
+      xs[j] = e < cap ? entry(e, qs[j]) : -1;
+      qs[j] = e < cap ? qs[j] : 0;
+      ys[j] = (e < cap && e + 1 < (qs[j] + 1) * k) ? entry(e + 1, q1) : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kUnionBatch; ++j) {
+      const int q = qs[j], x = xs[j], y = ys[j];
+      const bool vx = x >= 0 && x <= s_tq[q];
+      const bool vy = y >= 0 && y <= s_tq[q];
+#pragma unroll
+      for (int qq = 0; qq < QB; ++qq) nq[qq] += (vx && q == qq) ? 1u : 0u;
+      bad |= vy && (!vx || x >= y);
+      insert(x, q, 0);
     }
   }
-  bool one_seq = true;
 #pragma unroll
-  for (int q = 1; q < QB; ++q)
-    if (m * QB + q < total_q && s_bq[q] != s_bq[0]) one_seq = false;
+  for (int q = 0; q < QB; ++q) {
+    const uint32_t t = __builtin_amdgcn_readlane(wave_prefix_sum(nq[q]), kWave - 1);
+    if (lane == 0 && t != 0u) atomicAdd(&s_nq[q], (int)t);
+  }
+  if (__ballot(bad) != 0ull && lane == 0) s_bad = 1;
+  bool one_seq = true;
+  int tmax = -1;
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    if (q > 0 && m * QB + q < total_q && s_bq[q] != s_bq[0]) one_seq = false;
+    tmax = max(tmax, s_tq[q]);
+  }
   __syncthreads();
   if (s_bad != 0 || !one_seq) {
     // unused slots read a stand-in row that holds written data: position 0
@@ -891,78 +942,97 @@ __global__ __launch_bounds__(kUnionThreads) void mla_union_kernel(
       return;
     }
     const uint32_t safe = phys_row(block_table, bt_stride, s_bq[qs], 0u, page_size, pdiv, num_pages);
-    for (int e = tid; e < cap; e += kUnionThreads) {
-      const int q = (int)fast_div((uint32_t)e, kdiv);
-      const uint32_t x = s_a[e];
-      const bool valid = x != kSent;
-      u_rows[ubase + e] = valid ? phys_row(block_table, bt_stride, s_bq[q], x >> 3, page_size, pdiv,
-                                           num_pages)
-                                : safe;
-      u_mask[ubase + e] = valid ? (uint8_t)(1u << q) : (uint8_t)0;
+    for (int e0 = tid; e0 < cap; e0 += kUnionBatch * kUnionThreads) {
+      int xs[kUnionBatch], qv[kUnionBatch];
+#pragma unroll
+      for (int j = 0; j < kUnionBatch; ++j) {
+        const int e = e0 + j * kUnionThreads;
+        xs[j] = e < cap ? entry(e, qv[j]) : -1;
+        qv[j] = e < cap ? qv[j] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kUnionBatch; ++j) {
+        const int e = e0 + j * kUnionThreads;
+        if (e >= cap) continue;
+        const int q = qv[j], x = xs[j];
+        const bool valid = x >= 0 && x <= s_tq[q];
+        u_rows[ubase + e] = valid ? phys_row(block_table, bt_stride, s_bq[q], (uint32_t)x,
+                                             page_size, pdiv, num_pages)
+                                  : safe;
+        u_mask[ubase + e] = valid ? (uint8_t)(1u << q) : (uint8_t)0;
+      }
     }
     if (tid == 0) u_count[m] = cap;
     return;
   }
-  // merge rounds: lists of w rows at offsets p k (p a multiple of w), merged
-  // in pairs into lists of 2w rows at the left one's offset
-  uint32_t *src = s_a, *dst = s_b;
-  auto list_len = [&](int p, int w) {
-    int n = 0;
-    for (int q = p; q < p + w; ++q) n += s_nq[q];
-    return n;
-  };
+  const int32_t *bt_row = block_table + (int64_t)s_bq[0] * bt_stride;
+  uint32_t done = 0;  // slots written by earlier windows
+  for (int w0 = 0; w0 <= tmax; w0 += W) {
+    if (w0 > 0) {
+      // (the first window's map was filled by the count pass)
+      for (int i = tid; i < kWords / 4; i += kUnionThreads) m4[i] = u32x4_t{0u, 0u, 0u, 0u};
+      __syncthreads();
+      for (int e0 = tid; e0 < cap; e0 += kUnionBatch * kUnionThreads) {
+        int xs[kUnionBatch], qv[kUnionBatch];
 #pragma unroll
-  for (int w = 1; w < QB; w *= 2) {
-    for (int e = tid; e < cap; e += kUnionThreads) {
-      const int q = (int)fast_div((uint32_t)e, kdiv);
-      const int lst = q / w;
-      const int p = (lst & ~1) * w;  // first row of the pair's left list
-      const bool left = (lst & 1) == 0;
-      const int loff = p * k, roff = (p + w) * k;
-      const int nl = list_len(p, w), nr = list_len(p + w, w);
-      const int i = e - (left ? loff : roff);
-      if (i >= (left ? nl : nr)) continue;
-      const uint32_t x = src[e];
-      const uint32_t *po = src + (left ? roff : loff);
-      int lo = 0, hi = left ? nr : nl;  // keys below x in the partner list
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (po[mid] < x) lo = mid + 1;
-        else hi = mid;
+        for (int j = 0; j < kUnionBatch; ++j) {
+          const int e = e0 + j * kUnionThreads;
+          xs[j] = e < cap ? entry(e, qv[j]) : -1;
+          qv[j] = e < cap ? qv[j] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < kUnionBatch; ++j) insert(xs[j], qv[j], w0);
       }
-      dst[loff + i + lo] = x;
     }
+    // the window's pages [p0, p0 + np) of the sequence (np <= W / page size + 1)
+    const int wtop = min(w0 + W, tmax + 1) - 1;
+    const int p0 = (int)fast_div((uint32_t)w0, pdiv);
+    const int np = (int)fast_div((uint32_t)wtop, pdiv) - p0 + 1;
+    for (int i = tid; i < np; i += kUnionThreads)
+      s_pg[i] = (uint32_t)clamp_page(bt_row[p0 + i], num_pages);
     __syncthreads();
-    uint32_t *t = src;
-    src = dst;
-    dst = t;
-  }
-  // compaction: each thread takes a contiguous range of the merged list, and
-  // the run starts (new positions) get consecutive slots in order
-  const int N = list_len(0, QB);
-  const int per = (N + kUnionThreads - 1) / kUnionThreads;
-  const int e0 = min(N, tid * per), e1 = min(N, e0 + per);
-  uint32_t cnt = 0;
-  for (int e = e0; e < e1; ++e) cnt += (e == 0 || (src[e] >> 3) != (src[e - 1] >> 3)) ? 1u : 0u;
-  const uint32_t incl = wave_prefix_sum(cnt);
-  if (lane == kWave - 1) s_wsum[wv] = incl;
-  __syncthreads();
-  uint32_t slot = incl - cnt, total = 0;
+    // wave wv's quarter of the map, words [wv kWaveWords, (wv + 1) kWaveWords),
+    // read 64 consecutive words at a time; only words up to the last position
+    const int wlast = (wtop - w0) >> 2;
+    const int wbeg = wv * kWaveWords;
+    const int wend = min(wbeg + kWaveWords, wlast + 1);
+    uint32_t cnt = 0;
+    for (int c = wbeg; c < wend; c += kWave) {
+      const int wi = c + lane;
+      cnt += wi < wend ? (uint32_t)__popc(nonzero_bytes(s_map[wi])) : 0u;
+    }
+    const uint32_t wtot = wave_prefix_sum(cnt);
+    if (lane == kWave - 1) s_wsum[wv] = wtot;
+    __syncthreads();
+    uint32_t run = done, total = 0;
 #pragma unroll
-  for (int w = 0; w < kW; ++w) {
-    slot += w < wv ? s_wsum[w] : 0u;
-    total += s_wsum[w];
+    for (int w = 0; w < kW; ++w) {
+      run += w < wv ? s_wsum[w] : 0u;
+      total += s_wsum[w];
+    }
+    for (int c = wbeg; c < wend; c += kWave) {
+      const int wi = c + lane;
+      const uint32_t x = wi < wend ? s_map[wi] : 0u;
+      const uint32_t n = (uint32_t)__popc(nonzero_bytes(x));
+      const uint32_t incl = wave_prefix_sum(n);
+      uint32_t slot = run + incl - n;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t mk = (x >> (8 * j)) & 0xFFu;
+        if (mk != 0u) {
+          const uint32_t pos = (uint32_t)(w0 + 4 * wi + j);
+          const uint32_t pidx = fast_div(pos, pdiv);
+          u_rows[ubase + slot] = s_pg[pidx - p0] * (uint32_t)page_size + (pos - pidx * (uint32_t)page_size);
+          u_mask[ubase + slot] = (uint8_t)mk;
+          ++slot;
+        }
+      }
+      run += __builtin_amdgcn_readlane(incl, kWave - 1);
+    }
+    done += total;
+    __syncthreads();  // the map, page slice and wave totals are free for the next window
   }
-  for (int e = e0; e < e1; ++e) {
-    const uint32_t pos = src[e] >> 3;
-    if (e > 0 && (src[e - 1] >> 3) == pos) continue;
-    uint32_t mk = 0;
-    for (int e2 = e; e2 < N && (src[e2] >> 3) == pos; ++e2) mk |= 1u << (src[e2] & 7u);
-    u_rows[ubase + slot] = phys_row(block_table, bt_stride, s_bq[0], pos, page_size, pdiv, num_pages);
-    u_mask[ubase + slot] = (uint8_t)mk;
-    ++slot;
-  }
-  if (tid == 0) u_count[m] = (int32_t)total;
+  if (tid == 0) u_count[m] = (int32_t)done;
 }
 
 // Attention over a block's union: one workgroup per (block, group of 64 / QB
@@ -1237,7 +1307,7 @@ bool mla_qblock_supported(int32_t q_dtype, int32_t n_heads, int32_t d_latent, in
                           int32_t k) {
   if (q_dtype != DSA_BF16 || d_latent != kDL || d_rope != kDR) return false;
   if (!(n_heads == 8 || (n_heads >= 16 && n_heads <= kH && n_heads % 16 == 0))) return false;
-  return (int64_t)mla_qblock_qb(n_heads) * k <= kQbMaxCands;
+  return (int64_t)mla_qblock_qb(n_heads) * k <= kQbMaxSlots;
 }
 
 namespace {

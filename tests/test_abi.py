@@ -198,8 +198,9 @@ def _mla_qb(b=None, q=FAKE, qd=L.DSA_BF16, H=64, DL=512, DR=64, c=None, idx=FAKE
     (dict(out=FAKE + 4), 2), (dict(DR=32), 2), (dict(qd=L.DSA_F32), 3),
     (dict(ws=None), 4), (dict(wsb=16), 4), (dict(ws=FAKE + 8), 4),
     # head counts other than 8 or a multiple of 16 up to 64, other row widths,
-    # or unions over 16384 slots (QB k) are not supported
-    (dict(H=12), 5), (dict(H=128), 5), (dict(H=4), 5), (dict(k=4097), 5),
+    # or unions over 2^20 slots (QB k) are not supported
+    (dict(H=12), 5), (dict(H=128), 5), (dict(H=4), 5), (dict(k=(1 << 18) + 1), 5),
+    (dict(H=8, k=(1 << 17) + 1), 5),
     (dict(qd=L.DSA_F32, c=_cache(row_elems=576, dtype=L.DSA_F32)), 5),
     (dict(b=_batch(max_seq_len=1 << 29, bt_stride=(1 << 29) // 64)), 5),
 ])

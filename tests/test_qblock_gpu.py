@@ -11,7 +11,8 @@ checked against the oracle's sparse_mla on the same indices (1e-2 RMS, lse to
   page sizes 16, 64 and 128; k not a multiple of the 32-row tile;
 * the merge's fallback: caller lists with repeats, -1, positions past t and
   unsorted entries, and decode batches whose blocks span sequences;
-* a union longer than one row-table chunk; and the restart path (rows scaled
+* a union longer than one row-table chunk, positions past one 32K-position
+  membership window; and the restart path (rows scaled
   so late logits exceed the first tile's reference by more than the headroom).
 """
 
@@ -74,6 +75,14 @@ CASES = {
     "h8_topk": (small_variant(PREFILL, mla_heads=8, topk=256), "topk"),
     "h8_locality_k17": (small_variant(PREFILL, mla_heads=8, topk=17), "locality"),
     "h32_locality": (small_variant(PREFILL, mla_heads=32, topk=512), "locality"),
+    # positions past one 32K-position membership window of the union kernel
+    "h64_topk_L70000": (small_variant(PREFILL, batch=1, lens=(70000,), q_per_seq=(6,), topk=512),
+                        "topk"),
+    "h8_locality_L70000": (small_variant(PREFILL, batch=1, lens=(70000,), q_per_seq=(11,),
+                                         mla_heads=8, topk=300), "locality"),
+    # page size 4: windows of 2048 pages (8192 positions), the staged page slice full
+    "h16_topk_P4_L20000": (small_variant(PREFILL, batch=1, lens=(20000,), q_per_seq=(5,),
+                                         mla_heads=16, page_size=4, topk=256), "topk"),
 }
 
 
