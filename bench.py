@@ -392,14 +392,17 @@ def mla_routes(args, dsa, wl, dev):
         recipe = (f"blocks of {LOCALITY_BLOCK} queries drawing from {hot} shared pages "
                   f"({LOCALITY_UNION_RATIO} x one query's {wl.topk} positions)")
     torch.cuda.synchronize()
-    # union statistics of the blocks the blocked call forms
+    # union statistics of the blocks the blocked call forms (a block whose rows
+    # span sequences takes every entry as its own slot)
     qb = 8 if wl.mla_heads == 8 else 4
     a = indices.cpu().numpy()
+    seq_of = np.repeat(np.arange(wl.batch), inp.q_lens_host)
     union = sel = 0
     for m in range(0, T, qb):
         v = a[m:m + qb]
         v = v[v >= 0]
-        union += int(np.unique(v).size)
+        one_seq = len(set(seq_of[m:m + qb].tolist())) == 1
+        union += int(np.unique(v).size) if one_seq else int(v.size)
         sel += int(v.size)
     n_blocks = (T + qb - 1) // qb
     kv = dsa.PagedCache(inp.kv_cache[0])

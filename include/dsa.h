@@ -199,6 +199,13 @@ size_t dsa_sparse_mla_workspace_size(int32_t total_q, int32_t n_heads, int32_t d
  * listed twice counts twice. The scale is passed explicitly (the pages tie it
  * to 1/sqrt(192 + 64), not to the absorbed width). Accumulation is fp32.
  *
+ * bf16 with d_latent 512, d_rope 64 and 1..64 heads runs on the matrix
+ * cores, each tile of selected rows feeding 64 (query, head) columns; with
+ * fewer than 64 heads the missing columns are computed on zero queries, so a
+ * head-sharded share costs about what 64 heads cost (dsa_sparse_mla_fwd_qblocked
+ * fills the columns with other queries instead). Other shapes run on a
+ * plain kernel.
+ *
  *   q        device [total_q, n_heads, d_latent + d_rope], element type q_dtype
  *   kv       paged latent cache, row_elems == d_latent + d_rope, dtype == q_dtype
  *            (F32 or BF16)

@@ -178,7 +178,8 @@ dsa_status mla_layers(const dsa_batch *batch, int32_t n_layers, const void *cons
         (ly[l].lse != nullptr && !aligned(ly[l].lse, 4)))
       return DSA_ERR_SHAPE;
   }
-  const bool mfma_shape = q_dtype == DSA_BF16 && n_heads == 64 && d_latent == 512 && d_rope == 64;
+  const bool mfma_shape =
+      q_dtype == DSA_BF16 && n_heads <= 64 && d_latent == 512 && d_rope == 64;
   if (!mfma_shape && d_latent > 1024) return DSA_ERR_UNSUPPORTED;
   if (mfma_shape && k > dsa::mla_max_k()) return DSA_ERR_UNSUPPORTED;
   const size_t need = (size_t)n_layers * dsa::mla_workspace_bytes(bt.total_q, n_heads, d_latent, k);

@@ -413,7 +413,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     const int32_t *__restrict__ cu_q, int batch, int total_q, int max_seq_len, int64_t bt_stride,
     const MlaLayerArgs layers, int blocks_per_layer, int page_size, FastDiv pdiv,
     const int32_t *__restrict__ indices, int k, int n_splits, int rows_per_split,
-    float scale_log2, float *__restrict__ ws_acc, float *__restrict__ ws_ml) {
+    float scale_log2, float *__restrict__ ws_acc, float *__restrict__ ws_ml, int n_heads) {
   // ring of row tiles: tile i lives in stage i % kStages
   __shared__ __attribute__((aligned(1024))) uint8_t s_tiles[kStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) uint32_t s_rowid[kMaxRowsPerSplit + kTileN];
@@ -456,12 +456,15 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
   // a row loads it at once, beside the row table's round trips; the other
   // splits (same XCD) load it once their table is built, from the L2 that
   // the first one filled, so the row's HBM reads of it are not repeated.
+  // With fewer than 64 heads the missing heads' queries are zero (nothing is
+  // loaded for them) and their outputs are not written.
   u32x4_t qf[kSteps];
-  const uint16_t *qp = q + ((int64_t)row * kH + 16 * wv + j) * kD + 8 * g;
+  const bool q_head = 16 * wv + j < n_heads;
+  const uint16_t *qp = q + ((int64_t)row * n_heads + (q_head ? 16 * wv + j : 0)) * kD + 8 * g;
   const bool q_first = split == 0;
   if (q_first) {
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) qf[s] = ldg16(qp + 32 * s);
+    for (int s = 0; s < kSteps; ++s) qf[s] = q_head ? ldg16(qp + 32 * s) : u32x4_t{0u, 0u, 0u, 0u};
   }
 
   // Row table, first round trip: the selected positions of this thread's
@@ -543,7 +546,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
 
   if (!q_first) {
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) qf[s] = ldg16(qp + 32 * s);
+    for (int s = 0; s < kSteps; ++s) qf[s] = q_head ? ldg16(qp + 32 * s) : u32x4_t{0u, 0u, 0u, 0u};
   }
   if (tid < kMlaWaves) s_over[tid] = 0;
   // every compiler-visible load (query block, row table) has landed before the
@@ -617,15 +620,16 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int head = 16 * wv + 4 * g + r;
+      if (head >= n_heads) continue;
       const float l = s_ml[head][1];
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-      float *op = out + ((int64_t)row * kH + head) * kDL + j;
+      float *op = out + ((int64_t)row * n_heads + head) * kDL + j;
 #pragma unroll
       for (int nt = 0; nt < 32; ++nt) op[16 * nt] = o[nt][r] * inv;
     }
-    if (lse != nullptr && tid < kH) {
+    if (lse != nullptr && tid < n_heads) {
       const float m = s_ml[tid][0], l = s_ml[tid][1];
-      lse[(int64_t)row * kH + tid] = l > 0.0f ? m * kLn2 + logf(l) : -INFINITY;
+      lse[(int64_t)row * n_heads + tid] = l > 0.0f ? m * kLn2 + logf(l) : -INFINITY;
     }
   } else {
     // the split's accumulators in register order: value (nt, r) of lane l
@@ -655,7 +659,7 @@ constexpr int kCombineBlocksPerRow = kH * kDL / 8 / kCombineThreads;  // 16
 
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(
     int total_q, int n_splits, const float *__restrict__ ws_acc, const float *__restrict__ ws_ml,
-    const MlaLayerArgs layers) {
+    const MlaLayerArgs layers, int n_heads) {
   constexpr int kU = 8;
   const int per_layer = total_q * kCombineBlocksPerRow;
   const int layer = (int)(blockIdx.x / (unsigned)per_layer);
@@ -714,14 +718,17 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(
       a1[r] = s1v;
     }
   }
-  float *dst = out + ((int64_t)row * kH + head0) * kDL + dim;
+  // (heads past n_heads are the zero-query columns of a smaller head count)
+  float *dst = out + ((int64_t)row * n_heads + head0) * kDL + dim;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
+    if (head0 + r >= n_heads) continue;
     const float inv = Lsum[r] > 0.0f ? 1.0f / Lsum[r] : 0.0f;
     dst[r * kDL] = a0[r] * inv;
     dst[r * kDL + 256] = a1[r] * inv;
     if (lse != nullptr && nt == 0 && (l & 15) == 0)
-      lse[(int64_t)row * kH + head0 + r] = Lsum[r] > 0.0f ? M[r] * kLn2 + logf(Lsum[r]) : -INFINITY;
+      lse[(int64_t)row * n_heads + head0 + r] =
+          Lsum[r] > 0.0f ? M[r] * kLn2 + logf(Lsum[r]) : -INFINITY;
   }
 }
 
@@ -1182,14 +1189,16 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_qblock_kernel(
   }
 }
 
+// The MFMA kernel serves 1..64 heads: a workgroup's 64 columns are the
+// query's heads, any missing ones computed on zero queries and dropped.
 bool mfma_shape(int32_t q_dtype, int32_t n_heads, int32_t d_latent, int32_t d_rope) {
-  return q_dtype == DSA_BF16 && n_heads == kH && d_latent == kDL && d_rope == kDR;
+  return q_dtype == DSA_BF16 && n_heads >= 1 && n_heads <= kH && d_latent == kDL && d_rope == kDR;
 }
 
 }  // namespace
 
 int mla_num_splits(int32_t total_q, int32_t n_heads, int32_t d_latent, int32_t k) {
-  if (total_q <= 0 || n_heads != kH || d_latent != kDL) return 1;
+  if (total_q <= 0 || n_heads < 1 || n_heads > kH || d_latent != kDL) return 1;
   // enough workgroups for every CU, never slices shorter than kMinRowsPerSplit,
   // never more than kMaxRowsPerSplit rows (the per-split LDS row table)
   const int want = (256 + total_q - 1) / total_q;
@@ -1229,7 +1238,8 @@ hipError_t mla_scratch(void **ptr) {
 size_t mla_workspace_bytes(int32_t total_q, int32_t n_heads, int32_t d_latent, int32_t k) {
   const int s = mla_num_splits(total_q, n_heads, d_latent, k);
   if (s <= 1) return 0;
-  return (size_t)total_q * s * n_heads * (d_latent + 2) * sizeof(float);
+  // split partials are kept for all 64 columns of the MFMA kernel
+  return (size_t)total_q * s * kH * (d_latent + 2) * sizeof(float);
 }
 
 hipError_t launch_sparse_mla(const BatchArgs &bt, const MlaLayer *ly, int n_layers,
@@ -1245,7 +1255,7 @@ hipError_t launch_sparse_mla(const BatchArgs &bt, const MlaLayer *ly, int n_laye
     float *ws_acc = static_cast<float *>(workspace);
     float *ws_ml = ws_acc == nullptr
                        ? nullptr
-                       : ws_acc + (size_t)n_layers * bt.total_q * S * n_heads * d_latent;
+                       : ws_acc + (size_t)n_layers * bt.total_q * S * kH * kDL;
     const int64_t rows_padded = (int64_t)(bt.total_q + kXcds - 1) / kXcds * kXcds;
     const int64_t bpl = rows_padded * S;
     if (bpl * n_layers > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
@@ -1268,12 +1278,12 @@ hipError_t launch_sparse_mla(const BatchArgs &bt, const MlaLayer *ly, int n_laye
                        bt.block_table, bt.seq_lens, bt.cu_q, bt.batch, bt.total_q,
                        bt.max_seq_len, bt.bt_stride, la, (int)bpl, page_size,
                        make_fast_div((uint32_t)page_size), indices, k, S, per, scale_log2,
-                       ws_acc, ws_ml);
+                       ws_acc, ws_ml, n_heads);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     hipLaunchKernelGGL(mla_combine_kernel,
                        dim3((unsigned)((int64_t)bt.total_q * kCombineBlocksPerRow * n_layers)),
-                       dim3(kCombineThreads), 0, stream, bt.total_q, S, ws_acc, ws_ml, la);
+                       dim3(kCombineThreads), 0, stream, bt.total_q, S, ws_acc, ws_ml, la, n_heads);
     return hipGetLastError();
   }
   for (int l = 0; l < n_layers; ++l) {

@@ -58,6 +58,15 @@ SMALL_CASES = {
     "mla_mfma_k17": small_variant(BF16_DECODE, batch=3, lens=(300, 1000, 9), topk=17),
     "mla_mfma_k2047": small_variant(BF16_DECODE, batch=2, lens=(3000, 2071), q_per_seq=(2, 1),
                                     topk=2047),
+    # the MFMA MLA with fewer than 64 heads (zero-query columns): 8 heads over
+    # many splits, 40 heads (not a multiple of a wave's 16), 1 head with a
+    # partial tile
+    "mla_mfma_h8": small_variant(BF16_DECODE, batch=3, lens=(3000, 700, 90), mla_heads=8,
+                                 topk=1000),
+    "mla_mfma_h40": small_variant(BF16_DECODE, batch=2, lens=(900, 300), q_per_seq=(3, 1),
+                                  mla_heads=40, topk=200),
+    "mla_mfma_h1_k17": small_variant(BF16_DECODE, batch=2, lens=(300, 64), mla_heads=1,
+                                     topk=17),
 }
 
 
@@ -97,14 +106,15 @@ def test_indexshare_layers_reuse_one_topk(dev):
     assert not torch.equal(outs[0][0], outs[1][0])
 
 
-@pytest.mark.parametrize("name,n_layers", [("indexshare_b64", 3), ("tiny", 2)])
-def test_mla_layers_call_equals_one_call_per_layer(name, n_layers, dev):
+@pytest.mark.parametrize("name,n_layers,heads", [("indexshare_b64", 3, 64),
+                                                  ("indexshare_b64", 2, 24), ("tiny", 2, 8)])
+def test_mla_layers_call_equals_one_call_per_layer(name, n_layers, heads, dev):
     """IndexShare as one call over several layers is bit-identical to one call per
-    layer (MFMA path with splits; generic path), canaries past every output intact,
-    and lse may be left out."""
+    layer (MFMA path with splits, also with 24 heads; generic path), canaries past
+    every output intact, and lse may be left out."""
     wl = small_variant(name, batch=3, lens=(3000, 2100, 5000) if name != "tiny" else (256, 90, 17),
-                       topk=1024 if name != "tiny" else 64, n_layers=n_layers)
-    print(f"[mla-layers] {name} x{n_layers}", flush=True)
+                       topk=1024 if name != "tiny" else 64, n_layers=n_layers, mla_heads=heads)
+    print(f"[mla-layers] {name} x{n_layers} h{heads}", flush=True)
     inp = to_device(make_inputs(wl), dev)
     _, idx, ref = P.run_gpu(inp)
     T = inp.total_q
