@@ -676,15 +676,24 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     for (int e = 0; e < 16; ++e) acc1[m][e] = 0.0f;
 #pragma unroll
   for (int u = 0; u < QW; ++u) p0[u] = 0.0f;
+  // (the empty asm statements keep each epilogue in its N-tile's block, where
+  // the issue pattern interleaves it with the MFMAs; left alone, the compiler
+  // sinks it below the branches that follow, after the last MFMA)
+  auto pin = [](float (&p)[QW]) {
+#pragma unroll
+    for (int u = 0; u < QW; ++u) asm volatile("" : "+v"(p[u]));
+  };
   for (int blk = 0; blk < nblk; ++blk) {
     const u32x4_t *kb = kbuf[blk & 1];
     mma(kb, 0, acc0);
     epi(acc1, p1);
     phase_order();
+    pin(p1);
     if (blk > 0) store(blk - 1, p0, p1);
     mma(kb, 1, acc1);
     epi(acc0, p0);
     phase_order();
+    pin(p0);
     if (blk + 1 < nblk) {
       lstore((blk & 1) ^ 1);
       if (blk + 2 < nblk) {
