@@ -250,7 +250,9 @@ def _pmc_rows(run_dir: str, counter: str):
         key = r.get("Dispatch_Id") or r.get("Correlation_Id")
         name = r["Kernel_Name"]
         per.setdefault(key, [name, 0.0])[1] += float(r["Counter_Value"]) * 1024.0  # KiB
-    return list(per.values())
+    # in dispatch order
+    order = sorted(per, key=lambda k: (0, int(k)) if str(k).isdigit() else (1, str(k)))
+    return [per[k] for k in order]
 
 
 def traffic_summary(fetch_dir: str, write_dir: str, workload: str, calls_per_stage: dict,
@@ -263,8 +265,15 @@ def traffic_summary(fetch_dir: str, write_dir: str, workload: str, calls_per_sta
         copies = [v for n, v in rows if "copyBuffer" in n or "copy" in n.lower()]
         return max(copies) if copies else None
 
-    pf, pw = probe(fetch), probe(write)
-    f_scale = COPY_PROBE_BYTES / pf if pf else 1.0
+    def read_probe(rows):  # the read-stream probe over COPY_PROBE_BYTES: the run's last one
+        reads = [v for n, v in rows if "read_stream_kernel" in n]
+        return reads[-1] if reads else None
+
+    pf, pw, pr = probe(fetch), probe(write), read_probe(fetch)
+    # reads are scaled by what FETCH_SIZE gives for a plain read of known size
+    # (the kernels' traffic is reads like it); the copy's reading is kept for
+    # comparison. Writes are scaled by the copy's WRITE_SIZE.
+    f_scale = COPY_PROBE_BYTES / pr if pr else (COPY_PROBE_BYTES / pf if pf else 1.0)
     w_scale = COPY_PROBE_BYTES / pw if pw else 1.0
     kernels = {}
     for rows, field, scale in ((fetch, "fetch", f_scale), (write, "write", w_scale)):
@@ -290,11 +299,16 @@ def traffic_summary(fetch_dir: str, write_dir: str, workload: str, calls_per_sta
     d = {"workload": workload, "source_hash": kernel_source_hash(),
          "copy_probe_bytes": COPY_PROBE_BYTES,
          "copy_probe_measured": {"fetch": pf, "write": pw},
-         "scale": {"fetch": f_scale, "write": w_scale},
+         "read_probe_measured": {"fetch": pr},
+         "scale": {"fetch": f_scale, "write": w_scale,
+                   "fetch_source": "read probe" if pr else "copy",
+                   "fetch_from_copy": COPY_PROBE_BYTES / pf if pf else None},
          "kernels": out_k, "stages": stages, "commands": commands,
          "note": ("FETCH_SIZE / WRITE_SIZE in KiB per dispatch (x1024), median over the "
-                  "dispatches of each kernel, each scaled by copy_probe_bytes / the counter's "
-                  "reading for one device-to-device copy of copy_probe_bytes")}
+                  "dispatches of each kernel; FETCH_SIZE scaled by copy_probe_bytes / its "
+                  "reading for one plain read of copy_probe_bytes (dsa_bench_read), "
+                  "WRITE_SIZE by copy_probe_bytes / its reading for one device-to-device "
+                  "copy of copy_probe_bytes")}
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     json.dump(d, open(path, "w"), indent=1)
     print(json.dumps({k: v["bytes_per_call"] for k, v in stages.items()}))
@@ -723,6 +737,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+        read_stream_gbs(COPY_PROBE_BYTES, flush, stream, reps=1)  # FETCH_SIZE calibration
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, kp)
     print(json.dumps(line), flush=True)

@@ -407,7 +407,8 @@ __device__ __forceinline__ void mla_tile(const lds_u8 *tb, uint32_t vmask, const
   }
 }
 
-template <bool kOff32>
+// kFull: the query has all 64 heads (no zero columns, constant row stride).
+template <bool kOff32, bool kFull>
 __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ cu_q, int batch, int total_q, int max_seq_len, int64_t bt_stride,
@@ -459,8 +460,9 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
   // With fewer than 64 heads the missing heads' queries are zero (nothing is
   // loaded for them) and their outputs are not written.
   u32x4_t qf[kSteps];
-  const bool q_head = 16 * wv + j < n_heads;
-  const uint16_t *qp = q + ((int64_t)row * n_heads + (q_head ? 16 * wv + j : 0)) * kD + 8 * g;
+  const int nh = kFull ? kH : n_heads;
+  const bool q_head = kFull || 16 * wv + j < nh;
+  const uint16_t *qp = q + ((int64_t)row * nh + (q_head ? 16 * wv + j : 0)) * kD + 8 * g;
   const bool q_first = split == 0;
   if (q_first) {
 #pragma unroll
@@ -620,16 +622,16 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int head = 16 * wv + 4 * g + r;
-      if (head >= n_heads) continue;
+      if (!kFull && head >= nh) continue;
       const float l = s_ml[head][1];
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-      float *op = out + ((int64_t)row * n_heads + head) * kDL + j;
+      float *op = out + ((int64_t)row * nh + head) * kDL + j;
 #pragma unroll
       for (int nt = 0; nt < 32; ++nt) op[16 * nt] = o[nt][r] * inv;
     }
-    if (lse != nullptr && tid < n_heads) {
+    if (lse != nullptr && tid < nh) {
       const float m = s_ml[tid][0], l = s_ml[tid][1];
-      lse[(int64_t)row * n_heads + tid] = l > 0.0f ? m * kLn2 + logf(l) : -INFINITY;
+      lse[(int64_t)row * nh + tid] = l > 0.0f ? m * kLn2 + logf(l) : -INFINITY;
     }
   } else {
     // the split's accumulators in register order: value (nt, r) of lane l
@@ -657,6 +659,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
 constexpr int kCombineThreads = 256;
 constexpr int kCombineBlocksPerRow = kH * kDL / 8 / kCombineThreads;  // 16
 
+template <bool kFull>
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(
     int total_q, int n_splits, const float *__restrict__ ws_acc, const float *__restrict__ ws_ml,
     const MlaLayerArgs layers, int n_heads) {
@@ -719,15 +722,16 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(
     }
   }
   // (heads past n_heads are the zero-query columns of a smaller head count)
-  float *dst = out + ((int64_t)row * n_heads + head0) * kDL + dim;
+  const int nh = kFull ? kH : n_heads;
+  float *dst = out + ((int64_t)row * nh + head0) * kDL + dim;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    if (head0 + r >= n_heads) continue;
+    if (!kFull && head0 + r >= nh) continue;
     const float inv = Lsum[r] > 0.0f ? 1.0f / Lsum[r] : 0.0f;
     dst[r * kDL] = a0[r] * inv;
     dst[r * kDL + 256] = a1[r] * inv;
     if (lse != nullptr && nt == 0 && (l & 15) == 0)
-      lse[(int64_t)row * n_heads + head0 + r] =
+      lse[(int64_t)row * nh + head0 + r] =
           Lsum[r] > 0.0f ? M[r] * kLn2 + logf(Lsum[r]) : -INFINITY;
   }
 }
@@ -1272,7 +1276,9 @@ hipError_t launch_sparse_mla(const BatchArgs &bt, const MlaLayer *ly, int n_laye
       const uint64_t pool_bytes = (uint64_t)ly[l].kv.num_pages * (uint64_t)ly[l].kv.page_size * kRowBytes;
       off32 = off32 && pool_bytes + 4096 <= (1ull << 32);
     }
-    auto kern = off32 ? sparse_mla_bf16_kernel<true> : sparse_mla_bf16_kernel<false>;
+    const bool full = n_heads == kH;
+    auto kern = off32 ? (full ? sparse_mla_bf16_kernel<true, true> : sparse_mla_bf16_kernel<true, false>)
+                      : (full ? sparse_mla_bf16_kernel<false, true> : sparse_mla_bf16_kernel<false, false>);
     const int page_size = ly[0].kv.page_size;
     hipLaunchKernelGGL(kern, dim3((unsigned)(bpl * n_layers)), dim3(kMlaThreads), 0, stream,
                        bt.block_table, bt.seq_lens, bt.cu_q, bt.batch, bt.total_q,
@@ -1281,7 +1287,8 @@ hipError_t launch_sparse_mla(const BatchArgs &bt, const MlaLayer *ly, int n_laye
                        ws_acc, ws_ml, n_heads);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
-    hipLaunchKernelGGL(mla_combine_kernel,
+    auto ck = full ? mla_combine_kernel<true> : mla_combine_kernel<false>;
+    hipLaunchKernelGGL(ck,
                        dim3((unsigned)((int64_t)bt.total_q * kCombineBlocksPerRow * n_layers)),
                        dim3(kCombineThreads), 0, stream, bt.total_q, S, ws_acc, ws_ml, la, n_heads);
     return hipGetLastError();
