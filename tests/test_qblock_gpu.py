@@ -75,6 +75,8 @@ CASES = {
     "h8_topk": (small_variant(PREFILL, mla_heads=8, topk=256), "topk"),
     "h8_locality_k17": (small_variant(PREFILL, mla_heads=8, topk=17), "locality"),
     "h32_locality": (small_variant(PREFILL, mla_heads=32, topk=512), "locality"),
+    # three head groups per block (workgroups numbered (xcd, group, block))
+    "h48_topk": (small_variant(PREFILL, mla_heads=48, topk=160), "topk"),
     # positions past one 32K-position membership window of the union kernel
     "h64_topk_L70000": (small_variant(PREFILL, batch=1, lens=(70000,), q_per_seq=(6,), topk=512),
                         "topk"),
@@ -194,3 +196,25 @@ def test_qblocked_rejects_unsupported(dev):
     with pytest.raises(dsa.DSAError):  # 12 heads: neither 8 nor a multiple of 16
         dsa.sparse_mla_fwd_qblocked(P.batch_of(inp), inp.q_mla[0], dsa.PagedCache(inp.kv_cache[0]),
                                     idx, wl.d_latent, wl.scale)
+
+
+def test_qblocked_without_lse_and_empty_batch(dev):
+    """lse may be left out (out unchanged bit for bit); an empty batch is a no-op."""
+    inp_h = make_inputs(PREFILL)
+    inp = to_device(inp_h, dev)
+    _, idx, _ = P.run_gpu(inp)
+    wl = inp.wl
+    b = P.batch_of(inp)
+    kv = dsa.PagedCache(inp.kv_cache[0])
+    o1, l1 = dsa.sparse_mla_fwd_qblocked(b, inp.q_mla[0], kv, idx, wl.d_latent, wl.scale)
+    o2, l2 = dsa.sparse_mla_fwd_qblocked(b, inp.q_mla[0], kv, idx, wl.d_latent, wl.scale,
+                                         want_lse=False)
+    torch.cuda.synchronize()
+    assert l2 is None and torch.equal(o1, o2)
+    # sequences with no query row this step: total_q = 0
+    empty = dsa.Batch(inp.block_table, inp.seq_lens, torch.zeros_like(inp.cu_q), 0,
+                      inp.max_seq_len, 0)
+    q0 = inp.q_mla[0][:0]
+    o3, l3 = dsa.sparse_mla_fwd_qblocked(empty, q0, kv, idx[:0], wl.d_latent, wl.scale)
+    torch.cuda.synchronize()
+    assert o3.shape[0] == 0 and l3.shape[0] == 0
