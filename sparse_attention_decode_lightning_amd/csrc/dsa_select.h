@@ -12,8 +12,11 @@
 // consecutive candidates (one coalesced 256-byte load) and a wave's
 // candidates are one contiguous range.
 //  * Three radix levels (11, 11 and 10 bits) use three LDS histograms that are
-//    cleared before the first level, so a level costs one barrier: after it
-//    every wave scans the whole histogram itself and reaches the same digit.
+//    cleared before the first level. With eight or more waves one wave scans
+//    a level's histogram and hands the digit to the others through LDS (a
+//    second barrier, but one scan of the histogram instead of one per wave:
+//    the scans' LDS reads were the level's cost); with fewer waves each wave
+//    scans it itself, and a level costs one barrier.
 //    Bin b sits at word b + 4 (b / 32): lane l of a scanning wave owns bins
 //    [32 l, 32 l + 32) and reads them with 16-byte loads that no other lane of
 //    its group of eight shares a bank with.
@@ -124,6 +127,30 @@ __device__ __forceinline__ void wave_pick(const uint32_t *hist, uint32_t need, u
   rest = need - (above_l + s_i - h_i);
 }
 
+// The digit pick of one level: with many waves one wave scans the histogram
+// and hands the result to the others through LDS (one barrier instead of
+// every wave reading the whole histogram); with few waves each picks itself.
+template <int NB, int C, int NW>
+__device__ __forceinline__ void block_pick(const uint32_t *hist, uint32_t need_in, uint32_t *slot,
+                                           uint32_t &digit, uint32_t &rest, uint32_t &count) {
+  if constexpr (NW >= 8) {
+    if ((threadIdx.x >> 6) == 0) {
+      wave_pick<NB, C>(hist, need_in, digit, rest, count);
+      if ((threadIdx.x & 63) == 0) {
+        slot[0] = digit;
+        slot[1] = rest;
+        slot[2] = count;
+      }
+    }
+    __syncthreads();
+    digit = slot[0];
+    rest = slot[1];
+    count = slot[2];
+  } else {
+    wave_pick<NB, C>(hist, need_in, digit, rest, count);
+  }
+}
+
 // LDS of one selection: the three histograms and the packed per-wave counts.
 template <int NW, int R, int C1 = 1, int C2 = 1>
 struct alignas(16) SelectShared {
@@ -132,6 +159,7 @@ struct alignas(16) SelectShared {
   uint32_t hist2[C2 * kSelCopyWords];
   uint32_t hist3[kSelBinsWords];
   uint32_t cnt[NW];
+  uint32_t pick[3];  // digit, still needed, count: one wave's pick for the block
 };
 
 // Candidate index held by slice u of the calling lane (wave-major layout).
@@ -178,7 +206,7 @@ __device__ __forceinline__ void select_run(const uint32_t (&key)[R], int n, int 
     if (valid(u)) atomicAdd(&h1[sel_bin(key[u] >> 21)], 1u);
   __syncthreads();
   uint32_t d, need, count;
-  wave_pick<kSelBins, C1>(sh.hist1, (uint32_t)k, d, need, count);
+  block_pick<kSelBins, C1, NW>(sh.hist1, (uint32_t)k, sh.pick, d, need, count);
   uint32_t prefix = d << 21;
   int shift = 21;
   if (need != count) {
@@ -188,7 +216,7 @@ __device__ __forceinline__ void select_run(const uint32_t (&key)[R], int n, int 
       if (valid(u) && (key[u] >> 21) == d)
         atomicAdd(&h2[sel_bin((key[u] >> 10) & 2047u)], 1u);
     __syncthreads();
-    wave_pick<kSelBins, C2>(sh.hist2, need, d, need, count);
+    block_pick<kSelBins, C2, NW>(sh.hist2, need, sh.pick, d, need, count);
     prefix |= d << 10;
     shift = 10;
     if (need != count) {
@@ -198,7 +226,7 @@ __device__ __forceinline__ void select_run(const uint32_t (&key)[R], int n, int 
         if (valid(u) && (key[u] >> 10) == (prefix >> 10))
           atomicAdd(&sh.hist3[sel_bin(key[u] & 1023u)], 1u);
       __syncthreads();
-      wave_pick<kSelBins / 2>(sh.hist3, need, d, need, count);
+      block_pick<kSelBins / 2, 1, NW>(sh.hist3, need, sh.pick, d, need, count);
       prefix |= d;
       shift = 0;
     }
