@@ -480,15 +480,16 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
 // [rows x heads, 128] x [128, keys] followed by the per-head ReLU and weighted
 // head sum, and the same keys serve every row of the block. A workgroup of 8
 // waves keeps the query fragments of its rows in registers for its whole key
-// range and streams the keys through LDS in blocks of 64.
+// range and streams the keys through LDS in blocks of 128 (64 for 16 heads).
 //
 // Each wave owns 64 (query, head) rows as two 32-row M-tiles of
 // v_mfma_f32_32x32x16_bf16 (4, 2 or 1 queries for 16, 32 or 64 heads) and a
-// block is two 32-key N-tiles, 8 K-steps each. The 32x32 shape leaves room for
-// about five VALU ops under each 32-cycle MFMA, which the ReLU, weight and head
-// sum (two ops per accumulator element) fit: N-tile 0's MFMAs issue alongside
-// the previous block's N-tile 1 epilogue, N-tile 1's alongside N-tile 0's, so
-// the barrier between blocks never leaves the matrix core without work.
+// block is four (two) 32-key N-tiles, 8 K-steps each. The 32x32 shape leaves
+// room for about five VALU ops under each 32-cycle MFMA, which the ReLU,
+// weight and head sum (two ops per accumulator element) fit: each N-tile's
+// MFMAs issue alongside the previous N-tile's epilogue (the first one's
+// alongside the previous block's last), so the barrier between blocks never
+// leaves the matrix core without work.
 //
 // LDS rows are 256 B with their 16-byte chunks XOR-swizzled by the key's low
 // bits, so the 32 keys of one B fragment spread over all bank groups. A lane's
@@ -497,13 +498,15 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
 // query row stores 256 contiguous bytes.
 constexpr int kPfThreads = 512;
 constexpr int kPfWaves = kPfThreads / kWave;
-constexpr int kPfKeys = 64;                              // keys per LDS block
-constexpr int kPfChunks = kPfKeys * kIdxDim * 2 / 16;    // 16-byte chunks per block
-constexpr int kPfStage = kPfChunks / kPfThreads;         // staged chunks per thread
+// Keys per LDS block: 128 for 32 or 64 heads (half the barriers, staging
+// writes and score-store branches per key: 838 vs 865 us at the 4096-query
+// prefill), 64 for 16 heads (whose four query rows per wave leave no
+// registers for a fourth N-tile's staging).
+template <int H> constexpr int pf_block_keys() { return H == 16 ? 64 : 128; }
 
 
-// CONTIG: the page size is a multiple of kPfKeys, so each block of 64 keys is
-// 64 consecutive rows of one page, found with one (scalar) block-table read.
+// CONTIG: the page size is a multiple of the key block, so each block is
+// consecutive rows of one page, found with one (scalar) block-table read.
 template <int H, bool CONTIG>
 __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
@@ -513,6 +516,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     float *__restrict__ scores, int64_t ld, int keys_per_split, FastDiv pdiv) {
   constexpr int QW = 64 / H;           // query rows per wave
   constexpr int QB = kPfWaves * QW;    // query rows per workgroup
+  constexpr int KB = pf_block_keys<H>();                 // keys per LDS block
+  constexpr int kNT = KB / 32;                           // 32-key N-tiles per block
+  constexpr int kPfChunks = KB * kIdxDim * 2 / 16;       // 16-byte chunks per block
+  constexpr int kPfStage = kPfChunks / kPfThreads;       // staged chunks per thread
   __shared__ u32x4_t kbuf[2][kPfChunks];
 
   const int qblk = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
@@ -530,7 +537,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
   const int kbeg = split * keys_per_split;
   if (t_last < 0 || kbeg > t_last) return;
   const int kend = min(kbeg + keys_per_split, t_last + 1);
-  const int nblk = (kend - kbeg + kPfKeys - 1) / kPfKeys;
+  const int nblk = (kend - kbeg + KB - 1) / KB;
 
   // Row 32 * m + x of this wave is (query u = (32 m + x) / H, head (32 m + x) % H).
   // A fragments: lane (lh, lc) holds row 32 * m + lc, dims 16 * s + 8 * lh .. + 8.
@@ -567,11 +574,11 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
   const int64_t bt_row = (int64_t)b * bt_stride;
   u32x4_t stage[kPfStage];
   int btv[kPfStage];
-  auto key_pos = [&](int blk, int i) { return min(kbeg + blk * kPfKeys + kr0 + 32 * i, t_last); };
+  auto key_pos = [&](int blk, int i) { return min(kbeg + blk * KB + kr0 + 32 * i, t_last); };
   auto clamp_page = [&](int64_t page) { return dsa::clamp_page(page, num_pages); };
   auto bt_load = [&](int blk) {
     if constexpr (CONTIG) {
-      btv[0] = block_table[bt_row + (int)fast_div((uint32_t)(kbeg + blk * kPfKeys), pdiv)];
+      btv[0] = block_table[bt_row + (int)fast_div((uint32_t)(kbeg + blk * KB), pdiv)];
     } else {
 #pragma unroll
       for (int i = 0; i < kPfStage; ++i)
@@ -580,7 +587,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
   };
   auto gload = [&](int blk) {
     if constexpr (CONTIG) {
-      const int kb0 = kbeg + blk * kPfKeys;
+      const int kb0 = kbeg + blk * KB;
       const int pidx = (int)fast_div((uint32_t)kb0, pdiv);
       const int64_t page = clamp_page(btv[0]);
       const uint8_t *base = kdata + (page * page_size + (kb0 - pidx * page_size)) * (2 * kIdxDim);
@@ -642,8 +649,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
   };
   // Lanes l and l ^ 32 hold the two halves of a query's head sum for key
   // 32 n + (l & 31); the swap pairs tile 0's upper half with tile 1's lower.
-  auto store = [&](int blk, const float (&p0)[QW], const float (&p1)[QW]) {
-    const int pos = kbeg + blk * kPfKeys + lane;
+  // half h of block blk: keys 64 h .. 64 h + 63
+  auto store = [&](int blk, int half, const float (&p0)[QW], const float (&p1)[QW]) {
+    const int pos = kbeg + blk * KB + 64 * half + lane;
 #pragma unroll
     for (int u = 0; u < QW; ++u) {
       auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0[u]), __float_as_uint(p1[u]),
@@ -683,17 +691,30 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
 #pragma unroll
     for (int u = 0; u < QW; ++u) asm volatile("" : "+v"(p[u]));
   };
+  // (with 128-key blocks, N-tiles 2 and 3 repeat the pattern, and the
+  // block's first half is stored between them)
   for (int blk = 0; blk < nblk; ++blk) {
     const u32x4_t *kb = kbuf[blk & 1];
     mma(kb, 0, acc0);
     epi(acc1, p1);
     phase_order();
     pin(p1);
-    if (blk > 0) store(blk - 1, p0, p1);
+    if (blk > 0) store(blk - 1, kNT / 2 - 1, p0, p1);
     mma(kb, 1, acc1);
     epi(acc0, p0);
     phase_order();
     pin(p0);
+    if constexpr (kNT == 4) {
+      mma(kb, 2, acc0);
+      epi(acc1, p1);
+      phase_order();
+      pin(p1);
+      store(blk, 0, p0, p1);
+      mma(kb, 3, acc1);
+      epi(acc0, p0);
+      phase_order();
+      pin(p0);
+    }
     if (blk + 1 < nblk) {
       lstore((blk & 1) ^ 1);
       if (blk + 2 < nblk) {
@@ -704,7 +725,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     __syncthreads();
   }
   epi(acc1, p1);
-  store(nblk - 1, p0, p1);
+  store(nblk - 1, kNT / 2 - 1, p0, p1);
 }
 
 // Any element types and sizes: one thread per (query row, key position), fp32
@@ -769,18 +790,19 @@ template <int H>
 hipError_t launch_prefill(const BatchArgs &bt, const void *q_idx, const float *w,
                           const CacheArgs &keys, float *scores, int64_t ld, hipStream_t stream) {
   constexpr int QB = kPfWaves * (64 / H);
+  constexpr int KB = pf_block_keys<H>();
   const int qblocks = (bt.max_q + QB - 1) / QB;
-  const int kblocks = (bt.max_seq_len + kPfKeys - 1) / kPfKeys;
+  const int kblocks = (bt.max_seq_len + KB - 1) / KB;
   const int64_t units = (int64_t)qblocks * bt.batch;
   int splits = (int)std::min<int64_t>((kFillWorkgroups + units - 1) / units, kblocks);
   splits = std::max(splits, 1);
-  const int keys_per_split = ((kblocks + splits - 1) / splits) * kPfKeys;
+  const int keys_per_split = ((kblocks + splits - 1) / splits) * KB;
   splits = (bt.max_seq_len + keys_per_split - 1) / keys_per_split;
   if (splits > 65535 || bt.batch > 65535) return hipErrorInvalidConfiguration;
   dim3 grid(qblocks, splits, bt.batch);
   const FastDiv pdiv = make_fast_div((uint32_t)keys.page_size);
-  auto kernel = keys.page_size % kPfKeys == 0 ? indexer_prefill_kernel<H, true>
-                                              : indexer_prefill_kernel<H, false>;
+  auto kernel = keys.page_size % KB == 0 ? indexer_prefill_kernel<H, true>
+                                         : indexer_prefill_kernel<H, false>;
   hipLaunchKernelGGL(kernel, grid, dim3(kPfThreads), 0, stream, bt.block_table, bt.seq_lens,
                      bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len, bt.bt_stride,
                      static_cast<const uint16_t *>(q_idx), w,
