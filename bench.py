@@ -71,6 +71,10 @@ def parse():
                     help="no step: time dsa_sparse_mla_fwd and dsa_sparse_mla_fwd_qblocked on "
                          "the same selections (the library's top-k of the workload's scores, "
                          "or locality-shaped lists) and print one JSON line comparing them")
+    ap.add_argument("--group-route", action="store_true",
+                    help="no step: time the components of a two-pass exact token selection "
+                         "(16-key group maxima, their top-k, a per-row re-score of the chosen "
+                         "groups, a final top-k) beside the two-call route, one JSON line")
     ap.add_argument("--mla-heads", type=int, default=0,
                     help="with --mla-routes: MLA heads per query (a head-sharded share of the "
                          "workload's 64), default the workload's")
@@ -384,6 +388,78 @@ LOCALITY_BLOCK = 64
 LOCALITY_UNION_RATIO = 2.16
 
 
+def group_route(args, dsa, wl, dev):
+    """Components of an exact token route that never writes [T, L] scores.
+
+    The k-th largest maximum of 16-key groups bounds the row's k-th score from
+    below, so only the k groups with the largest maxima can hold top-k tokens.
+    Proxies: pass 1 is the page-max indexer (page maxima instead of group
+    maxima); the group top-k and the final top-k are the top-k call on rows of
+    L/16 and 16k random scores; pass 2 is the indexer on 16k keys per query row
+    (each row re-scores its own groups), and on 16k keys shared by a
+    sequence's queries (the bound if they chose the same groups).
+    """
+    from workloads import make_inputs
+
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.ones(1 << 27, dtype=torch.int64, device=dev)
+
+    def timed(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        return round(float(np.median(ts)), 1)
+
+    def setup(w):
+        inp = make_inputs(w, device="cuda", poison=False)
+        batch = dsa.Batch(inp.block_table, inp.seq_lens, inp.cu_q, inp.total_q,
+                          inp.max_seq_len, inp.max_q)
+        return inp, batch, dsa.PagedCache(inp.k_cache, inp.k_scale)
+
+    k = wl.topk
+    res = {}
+    inp, batch, keys = setup(wl)
+    T, L, nq = inp.total_q, inp.max_seq_len, inp.max_q
+    sc = torch.empty((T, L), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(dsa.topk_workspace_size(T, L, k), 16), dtype=torch.uint8, device=dev)
+    res["indexer_us"] = timed(lambda: dsa.indexer_scores(batch, inp.q_idx, inp.w, keys, scores=sc))
+    res["topk_us"] = timed(lambda: dsa.topk(batch, sc, k, indices=idx, workspace=ws))
+    pg = torch.empty((T, -(-L // wl.page_size)), dtype=torch.float32, device=dev)
+    res["pass1_page_max_indexer_us"] = timed(
+        lambda: dsa.indexer_page_scores(batch, inp.q_idx, inp.w, keys, wl.page_size, out=pg))
+    del inp, batch, keys, sc
+    torch.cuda.empty_cache()
+    gen = torch.Generator(device="cuda").manual_seed(wl.seed)
+    for name, n in (("group_topk_us", L // 16), ("final_topk_us", 16 * k)):
+        inp, batch, keys = setup(wl.replace(batch=T, q_per_seq=1, lens=n))
+        s2 = torch.randn((T, n), generator=gen, device=dev)
+        i2 = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w2 = torch.empty(max(dsa.topk_workspace_size(T, n, k), 16), dtype=torch.uint8, device=dev)
+        res[name] = timed(lambda: dsa.topk(batch, s2, k, indices=i2, workspace=w2))
+        if name == "final_topk_us":
+            res["pass2_per_row_us"] = timed(
+                lambda: dsa.indexer_scores(batch, inp.q_idx, inp.w, keys, scores=s2))
+        del inp, batch, keys
+        torch.cuda.empty_cache()
+    inp, batch, keys = setup(wl.replace(batch=T // nq, q_per_seq=nq, lens=16 * k))
+    s4 = torch.empty((T, 16 * k), dtype=torch.float32, device=dev)
+    res["pass2_shared_us"] = timed(lambda: dsa.indexer_scores(batch, inp.q_idx, inp.w, keys, scores=s4))
+    res["two_call_us"] = round(res["indexer_us"] + res["topk_us"], 1)
+    res["group_route_us"] = [round(res["pass1_page_max_indexer_us"] + res["group_topk_us"]
+                                   + res[p] + res["final_topk_us"], 1)
+                             for p in ("pass2_shared_us", "pass2_per_row_us")]
+    print(json.dumps({"workload": wl.name, "rows": T, "L": L, "k": k, **res}))
+
+
 def mla_routes(args, dsa, wl, dev):
     from workloads import locality_indices, make_inputs, small_variant
 
@@ -510,6 +586,9 @@ def main():
     wl = WORKLOADS[args.workload]
     if args.mla_routes:
         mla_routes(args, dsa, wl, dev)
+        return
+    if args.group_route:
+        group_route(args, dsa, wl, dev)
         return
     inp = make_inputs(wl, device="cuda")
     T = inp.total_q
