@@ -71,6 +71,9 @@ def parse():
                     help="no step: time dsa_sparse_mla_fwd and dsa_sparse_mla_fwd_qblocked on "
                          "the same selections (the library's top-k of the workload's scores, "
                          "or locality-shaped lists) and print one JSON line comparing them")
+    ap.add_argument("--fused-topk", action="store_true",
+                    help="score and select in one dsa_indexer_topk launch (one query row per "
+                         "sequence, rows of up to 16K positions) instead of two calls")
     ap.add_argument("--group-route", action="store_true",
                     help="no step: time the components of a two-pass exact token selection "
                          "(16-key group maxima, their top-k, a per-row re-score of the chosen "
@@ -628,7 +631,12 @@ def main():
             fused = True
         except dsa.DSAError:
             fused = False
-    sel_names = (["page_topk"] if fused else ["page_scores", "page_topk"]) if kp else ["topk"]
+    fused_topk = bool(args.fused_topk) and not kp
+    if fused_topk:
+        tk_state = torch.zeros(max(dsa.indexer_topk_state_size(T), 16), dtype=torch.uint8,
+                               device=dev)
+    sel_names = ((["page_topk"] if fused else ["page_scores", "page_topk"]) if kp else
+                 ([] if fused_topk else ["topk"]))
     mla_calls = 1 if layered else wl.n_layers
     n_ev = 2 + len(sel_names) + mla_calls
 
@@ -638,6 +646,9 @@ def main():
             evs[e].record(stream)
         if fused:
             dsa.indexer_page_scores(batch, inp.q_idx, inp.w, keys, page, out=page_sc)
+        elif fused_topk:
+            dsa.indexer_topk(batch, inp.q_idx, inp.w, keys, wl.topk, scores=scores,
+                             indices=indices, state=tk_state)
         else:
             dsa.indexer_scores(batch, inp.q_idx, inp.w, keys, scores=scores)
         e += 1
@@ -651,11 +662,12 @@ def main():
         if kp:
             dsa.page_topk(batch, page_sc, page, kp, pages=pages_sel, indices=indices,
                           workspace=pk_ws)
-        else:
+        elif not fused_topk:
             dsa.topk(batch, scores, wl.topk, indices=indices, workspace=tk_ws)
-        e += 1
-        if evs is not None:
-            evs[e].record(stream)
+        if not fused_topk:
+            e += 1
+            if evs is not None:
+                evs[e].record(stream)
         if layered:
             dsa.sparse_mla_fwd_layers(batch, inp.q_mla, kvs, indices, wl.d_latent, wl.scale,
                                       outs=outs, lses=lses, workspace=ws)
@@ -731,12 +743,14 @@ def main():
     warm_ms = w0.elapsed_time(w1) / args.steps
 
     ab = algorithmic_bytes(inp, k_sel=k_sel, page=page if kp else 0, fused=fused)
-    names = ["indexer"] + sel_names + ([f"mla_{wl.n_layers}_layers"] if layered else
+    names = ["indexer_topk" if fused_topk else "indexer"] + sel_names + (
+        [f"mla_{wl.n_layers}_layers"] if layered else
                                        [f"mla_l{l}" for l in range(wl.n_layers)])
     n_sel = len(sel_names)
     mla_ms = float(np.sum(stage_ms[1 + n_sel:]))
     sel_ms = float(np.sum(stage_ms[1:1 + n_sel]))
-    kern = {"indexer": (float(stage_ms[0]), ab["indexer"], "dsa_indexer_scores",
+    kern = {"indexer": (float(stage_ms[0]), ab["indexer"] + (ab["topk"] if fused_topk else 0),
+                        "dsa_indexer_topk" if fused_topk else "dsa_indexer_scores",
                         ab["flops_indexer"]),
             "topk": (sel_ms, ab["topk"], "dsa_page_topk" if kp else "dsa_topk", 0),
             # one call: one layer, or every layer through dsa_sparse_mla_fwd_layers
@@ -789,7 +803,8 @@ def main():
                    "page_size": wl.page_size, "mla_layers": wl.n_layers,
                    "selection": (f"page budget: {kp} pages of {page} positions"
                                  + (", page maxima from the indexer" if fused else "") if kp
-                                 else f"token top-{wl.topk}"),
+                                 else f"token top-{wl.topk}"
+                                 + (", fused into the indexer launch" if fused_topk else "")),
                    "parallelism": "single GPU"},
         "achieved_hbm_gbs": ab["total"] / (ms * 1e-3) / 1e9,
         "algorithmic_bytes_per_step": ab["total"],

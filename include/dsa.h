@@ -179,6 +179,51 @@ size_t dsa_topk_workspace_size(int32_t total_q, int32_t max_seq_len, int32_t k);
 dsa_status dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld_scores, int32_t k,
                     int32_t *indices, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of the per-row state dsa_indexer_topk keeps between calls. */
+size_t dsa_indexer_topk_state_size(int32_t total_q);
+
+/*
+ * The indexer and the top-k in one launch ("Making GLM-5.2 Sparse on TPUs",
+ * section "Stream indexer scores over live context": the selection is fed
+ * from the streaming indexer; section "What the stack now delivers": token
+ * top-k over few rows is the latency to cut).
+ *
+ * Equal to dsa_indexer_scores followed by dsa_topk with the same k: the same
+ * scores in `scores` and bit-identical indices. The workgroups that score a
+ * row also count their scores' top 11 key bits into the row's histogram in
+ * `state`, and the row's last workgroup to finish (an atomic count; no
+ * workgroup waits for another) selects the row from that histogram and the
+ * scores, so the selection needs no pass of its own over the row.
+ *
+ * Supported for decode rows: at most one query row per sequence (max_q <= 1),
+ * bf16 queries, head_dim 128, 16, 32 or 64 heads, bf16 or fp8 keys in pages
+ * of a multiple of 64 rows, max_seq_len <= 16384; otherwise
+ * DSA_ERR_UNSUPPORTED (the two-call route covers every case). On MI355X the
+ * two calls are faster on every shape measured (1 to 32 rows of 2K to 16K
+ * positions): the final selection runs on the row's one four-wave workgroup
+ * instead of a 16-wave one, and each workgroup's device-scope release costs
+ * more than the launch it saves. Rows that no sequence's query range holds
+ * are not written.
+ *
+ *   scores  device [total_q, ld_scores] fp32, written as by dsa_indexer_scores
+ *   indices device [total_q, k] int32, written as by dsa_topk
+ *   state   device, >= dsa_indexer_topk_state_size(total_q) bytes, 256-byte
+ *           aligned. It must be zero-filled before its first use (one
+ *           hipMemset after allocation); every call that completes leaves
+ *           the part it used zero-filled again, so one state buffer serves
+ *           every later call with as many rows or fewer. Calls that overlap
+ *           in time (other streams) need separate state buffers. The caller
+ *           owns it.
+ *
+ * Errors: as for the two calls; DSA_ERR_WORKSPACE for a missing, short or
+ * misaligned state; DSA_ERR_UNSUPPORTED outside the shapes above.
+ */
+dsa_status dsa_indexer_topk(const dsa_batch *batch, const void *q_idx, int32_t q_dtype,
+                            const float *w, int32_t n_heads, int32_t head_dim,
+                            const dsa_paged_cache *keys, int32_t k, float *scores,
+                            int64_t ld_scores, int32_t *indices, void *state,
+                            size_t state_bytes, void *stream);
+
 /* Bytes of workspace dsa_sparse_mla_fwd needs for these host bounds. */
 size_t dsa_sparse_mla_workspace_size(int32_t total_q, int32_t n_heads, int32_t d_latent,
                                      int32_t k);

@@ -34,6 +34,7 @@ __all__ = [
     "topk_workspace_size", "sparse_mla_workspace_size", "abi_version", "kv_append",
     "page_scores", "page_topk", "page_topk_workspace_size", "indexer_page_scores",
     "sparse_mla_fwd_noalloc", "sparse_mla_fwd_qblocked", "sparse_mla_qblocked_workspace_size",
+    "indexer_topk", "indexer_topk_state_size",
 ]
 
 _DT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.uint8: DSA_FP8_E4M3,
@@ -216,6 +217,46 @@ def indexer_page_scores(batch: Batch, q_idx: torch.Tensor, w: torch.Tensor, keys
                                       out.shape[1], _stream(q_idx.device)),
           "dsa_indexer_page_scores")
     return out
+
+
+def indexer_topk_state_size(total_q: int) -> int:
+    return int(lib.dsa_indexer_topk_state_size(total_q))
+
+
+def indexer_topk(batch: Batch, q_idx: torch.Tensor, w: torch.Tensor, keys: PagedCache, k: int,
+                 scores: Optional[torch.Tensor] = None, indices: Optional[torch.Tensor] = None,
+                 state: Optional[torch.Tensor] = None):
+    """(scores [T, ld], indices [T, k]): indexer_scores then topk in one launch (decode rows
+    of the streamed-key configurations; DSAError(UNSUPPORTED) otherwise). `state` must be
+    zero-filled before its first call and is zero-filled again after each call; a new one is
+    made when it is None."""
+    T, H, D = q_idx.shape
+    qd = _DT.get(q_idx.dtype)
+    if qd not in (DSA_F32, DSA_BF16):
+        raise TypeError("q_idx must be float32 or bfloat16")
+    if tuple(w.shape) != (T, H):
+        raise ValueError("w must be [T, n_heads]")
+    _rows(q_idx, "q_idx", batch)
+    dev = q_idx.device
+    if scores is None:
+        scores = torch.empty((T, max(1, batch.max_seq_len)), dtype=torch.float32, device=dev)
+    if scores.dim() != 2 or scores.shape[0] != T or scores.shape[1] < batch.max_seq_len:
+        raise ValueError("scores must be [T, ld] with ld >= max_seq_len")
+    if indices is None:
+        indices = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if tuple(indices.shape) != (T, k):
+        raise ValueError("indices must be [T, k]")
+    need = indexer_topk_state_size(batch.total_q)
+    if state is None:
+        state = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+    b, kc = batch.c(), keys.c()
+    check(lib.dsa_indexer_topk(ctypes.byref(b), _dev(q_idx, "q_idx"), qd,
+                               _dev(w, "w", torch.float32), H, D, ctypes.byref(kc), k,
+                               _dev(scores, "scores", torch.float32), scores.shape[1],
+                               _dev(indices, "indices", torch.int32), _dev(state, "state"),
+                               state.numel() * state.element_size(), _stream(dev)),
+          "dsa_indexer_topk")
+    return scores, indices
 
 
 def page_topk_workspace_size(total_q: int, max_seq_len: int, page_size: int, kp: int) -> int:

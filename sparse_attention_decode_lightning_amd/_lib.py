@@ -89,6 +89,10 @@ def _load():
                                               P, SZ, P]
     lib.dsa_indexer_page_scores.restype = ctypes.c_int
     lib.dsa_indexer_page_scores.argtypes = [BP, P, I32, P, I32, I32, CP, I32, P, I64, P]
+    lib.dsa_indexer_topk_state_size.restype = SZ
+    lib.dsa_indexer_topk_state_size.argtypes = [I32]
+    lib.dsa_indexer_topk.restype = ctypes.c_int
+    lib.dsa_indexer_topk.argtypes = [BP, P, I32, P, I32, I32, CP, I32, P, I64, P, P, SZ, P]
     lib.dsa_page_scores.restype = ctypes.c_int
     lib.dsa_page_scores.argtypes = [BP, P, I64, I32, P, I64, P]
     lib.dsa_page_topk_workspace_size.restype = SZ

@@ -306,6 +306,40 @@ dsa_status dsa_indexer_page_scores(const dsa_batch *batch, const void *q_idx, in
                                                        static_cast<hipStream_t>(stream)));
 }
 
+size_t dsa_indexer_topk_state_size(int32_t total_q) {
+  return dsa::indexer_topk_state_bytes(total_q);
+}
+
+dsa_status dsa_indexer_topk(const dsa_batch *batch, const void *q_idx, int32_t q_dtype,
+                            const float *w, int32_t n_heads, int32_t head_dim,
+                            const dsa_paged_cache *keys, int32_t k, float *scores,
+                            int64_t ld_scores, int32_t *indices, void *state,
+                            size_t state_bytes, void *stream) {
+  BatchArgs bt;
+  CacheArgs kc;
+  dsa_status st = check_batch(batch, &bt);
+  if (st != DSA_OK) return st;
+  if (keys == nullptr) return DSA_ERR_NULL;
+  if (bt.total_q > 0 &&
+      (q_idx == nullptr || w == nullptr || scores == nullptr || indices == nullptr))
+    return DSA_ERR_NULL;
+  st = check_cache(keys, bt, &kc);
+  if (st != DSA_OK) return st;
+  if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (n_heads < 1 || head_dim < 1 || kc.row_elems != head_dim || k < 1) return DSA_ERR_SHAPE;
+  if (ld_scores < bt.max_seq_len || ld_scores < 1) return DSA_ERR_SHAPE;
+  if (!aligned(q_idx, 16) || !aligned(w, 4) || !aligned(scores, 4) || !aligned(indices, 4))
+    return DSA_ERR_SHAPE;
+  if (!dsa::indexer_topk_supported(bt, q_dtype, n_heads, head_dim, kc)) return DSA_ERR_UNSUPPORTED;
+  const size_t need = dsa::indexer_topk_state_bytes(bt.total_q);
+  if (need > 0 && (state == nullptr || state_bytes < need || !aligned(state, 256)))
+    return DSA_ERR_WORKSPACE;
+  if (bt.total_q == 0) return DSA_OK;
+  return launch_status(dsa::launch_indexer_topk(bt, q_idx, w, n_heads, kc, k, indices, scores,
+                                                ld_scores, static_cast<uint32_t *>(state),
+                                                static_cast<hipStream_t>(stream)));
+}
+
 dsa_status dsa_page_scores(const dsa_batch *batch, const float *scores, int64_t ld_scores,
                            int32_t page_size, float *page_scores, int64_t ld_pages, void *stream) {
   BatchArgs bt;

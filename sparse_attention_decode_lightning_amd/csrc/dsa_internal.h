@@ -46,6 +46,16 @@ hipError_t launch_indexer_page_scores(const BatchArgs &bt, const void *q_idx, co
                                       int32_t n_heads, const CacheArgs &keys, int32_t sel_page,
                                       float *page_scores, int64_t ld_pages, hipStream_t stream);
 
+// Indexer scores and their top-k in one launch (one query row per sequence,
+// streamed keys, rows of up to 16K positions); `state` is zero between calls.
+bool indexer_topk_supported(const BatchArgs &bt, int32_t q_dtype, int32_t n_heads,
+                            int32_t head_dim, const CacheArgs &keys);
+size_t indexer_topk_state_bytes(int32_t total_q);
+hipError_t launch_indexer_topk(const BatchArgs &bt, const void *q_idx, const float *w,
+                               int32_t n_heads, const CacheArgs &keys, int32_t k,
+                               int32_t *indices, float *scores, int64_t ld_scores,
+                               uint32_t *state, hipStream_t stream);
+
 size_t topk_workspace_bytes(int32_t total_q, int32_t max_cands, int32_t k);
 bool topk_supported(int32_t max_cands, int32_t k);
 // expand (page candidates only): also write the kept pages' positions there

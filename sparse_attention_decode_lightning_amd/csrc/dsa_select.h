@@ -181,9 +181,13 @@ __device__ __forceinline__ void select_clear(Sh &sh) {
 // The k best of the n candidates sel_cand(u) < n (n > k): emit(u, slot) is
 // called once for every kept candidate, with its slot in [0, k) of the
 // ascending-candidate list. Every thread of the block must call it.
-template <int NW, int R, int C1, int C2, typename Emit>
+// kH1Given: the caller has already filled hist1 (one copy) with the level-1
+// counts of exactly these n keys, e.g. summed over the workgroups that
+// produced them, and the level-1 pass is skipped.
+template <bool kH1Given = false, int NW, int R, int C1, int C2, typename Emit>
 __device__ __forceinline__ void select_run(const uint32_t (&key)[R], int n, int k,
                                            SelectShared<NW, R, C1, C2> &sh, Emit emit) {
+  static_assert(!kH1Given || C1 == 1, "a given level-1 histogram has one copy");
   static_assert(NW * R * kWave < 65536, "16-bit packed counts");
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -201,10 +205,12 @@ __device__ __forceinline__ void select_run(const uint32_t (&key)[R], int n, int 
   uint32_t *h2 = sh.hist2 + (lane % C2) * kSelCopyWords;
 
   // level 1: bits 31..21
+  if constexpr (!kH1Given) {
 #pragma unroll
-  for (int u = 0; u < R; ++u)
-    if (valid(u)) atomicAdd(&h1[sel_bin(key[u] >> 21)], 1u);
-  __syncthreads();
+    for (int u = 0; u < R; ++u)
+      if (valid(u)) atomicAdd(&h1[sel_bin(key[u] >> 21)], 1u);
+    __syncthreads();
+  }
   uint32_t d, need, count;
   block_pick<kSelBins, C1, NW>(sh.hist1, (uint32_t)k, sh.pick, d, need, count);
   uint32_t prefix = d << 21;

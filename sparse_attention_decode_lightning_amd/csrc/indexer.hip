@@ -20,6 +20,7 @@
 
 #include "dsa_device.h"
 #include "dsa_internal.h"
+#include "dsa_select.h"
 
 namespace dsa {
 namespace {
@@ -164,6 +165,9 @@ constexpr int kStreamBlocks = 16;  // blocks of scores buffered in LDS between w
 constexpr int kStreamWorkgroups = 512;
 constexpr int kStreamStages = 4;
 constexpr int kStreamKeys = 64;
+constexpr int kFusedHistOff = 64;                       // words: the count, then padding
+constexpr int kFusedRowWords = kFusedHistOff + kSelBins;  // per row, 256-byte multiple
+static_assert(kSelBins == 8 * 256, "eight bins per thread of a 256-thread workgroup");
 
 // Direct global-to-LDS copy, 16 (or 4) bytes per lane, at lds + 16 l (4 l).
 // Issued as inline assembly so the compiler's automatic waits ignore it;
@@ -197,18 +201,31 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Fused top-k state of one query row: the count of the row's workgroups that
+// have finished, then (from word kFusedHistOff) the row's level-1 histogram.
+struct FusedTopk {
+  int k;
+  int32_t *indices;  // [total_q, k]
+  uint32_t *state;   // [total_q, kFusedRowWords], zero between calls
+};
+
 // PMAX: instead of the token scores, each row's page maxima over logical
 // pages of one 64-key block (the selection's pages):
 // scores[row * ld + page] = max of the page's scores at positions <= t (pages
 // wholly past t are not written).
-template <int NMT, int QG, bool FP8, bool PMAX>
+// TR > 0 (one query row per workgroup, runs of at most kStreamBlocks blocks):
+// the scores are written as without it, and the row's top-k goes to
+// tk.indices, selected by the row's last workgroup to finish; TR is the
+// candidates per lane of that selection (rows of up to 256 TR positions).
+template <int NMT, int QG, bool FP8, bool PMAX, int TR = 0>
 __global__ __launch_bounds__(256) void indexer_stream_kernel(
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ cu_q, int batch, int total_q, int max_seq_len, int64_t bt_stride,
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
     const uint8_t *__restrict__ kdata, const float *__restrict__ kscale, int64_t num_pages,
     int page_size, FastDiv pdiv, float *__restrict__ scores, int64_t ld, int run_blocks,
-    int page_blocks) {
+    int page_blocks, FusedTopk tk) {
+  static_assert(TR == 0 || (QG == 1 && !PMAX), "fused selection: one row per workgroup");
   constexpr int H = NMT * 16;
   constexpr int RB = FP8 ? kIdxDim : 2 * kIdxDim;    // bytes per key row
   constexpr int CPK = RB / 16;                      // 16-byte chunks per key
@@ -234,7 +251,14 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
   const int t_first = L - qn + i0;
   const int t_last = t_first + nq - 1;
   const int key0 = chunk * run_blocks * kStreamKeys;
-  if (t_last < 0 || key0 > t_last) return;
+  if (t_last < 0 || key0 > t_last) {
+    if constexpr (TR > 0) {
+      // a row with no position: its first workgroup writes the empty list
+      if (t_last < 0 && chunk == 0)
+        for (int i = tid; i < tk.k; i += 256) tk.indices[(int64_t)(q0 + i0) * tk.k + i] = -1;
+    }
+    return;
+  }
   const int nblk = min(run_blocks, (t_last - key0) / kStreamKeys + 1);
 
   // Four query rows of 32 heads (draft verification) take the wide path:
@@ -472,6 +496,68 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
       }
       lds_barrier();
     }
+  }
+  if constexpr (TR > 0) {
+    // The run's scores are still in s_out[0]. Count their level-1 digits,
+    // add the counts to the row's histogram, and count this workgroup in:
+    // the row's last workgroup to arrive has every score and every count,
+    // and selects the row. No workgroup waits for another.
+    using Sh = SelectShared<4, TR>;
+    static_assert(sizeof(Sh) <= sizeof(s_st), "the selection reuses the stage buffers");
+    Sh &sh = *reinterpret_cast<Sh *>(&s_st[0][0]);
+    __shared__ uint32_t s_last;
+    const int64_t row = q0 + i0;
+    const int nrun = min(nblk * kStreamKeys, t_last + 1 - key0);  // positions of this run
+    uint32_t *st = tk.state + row * kFusedRowWords;
+    uint32_t *gh = st + kFusedHistOff;
+    select_clear(sh);
+    __syncthreads();
+    for (int i = tid; i < nrun; i += 256)
+      atomicAdd(&sh.hist1[sel_bin(order_key(s_out[0][i]) >> 21)], 1u);
+    __syncthreads();
+    for (int bin = tid; bin < kSelBins; bin += 256) {
+      const uint32_t c = sh.hist1[sel_bin(bin)];
+      if (c != 0u) atomicAdd(gh + bin, c);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this run's scores and counts, then the arrival
+    __syncthreads();
+    const int parts = t_last / (run_blocks * kStreamKeys) + 1;  // workgroups of the row
+    if (tid == 0) s_last = atomicAdd(st, 1u) == (uint32_t)(parts - 1) ? 1u : 0u;
+    __syncthreads();
+    if (s_last == 0u) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other runs' scores and counts
+    // the row's histogram into LDS (hist2 and hist3 cleared), and the state
+    // cleared for the next call
+    select_clear(sh);
+    __syncthreads();
+    {
+      const int b8 = 8 * tid;  // bins b8 .. b8 + 7, one padded run of LDS words
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(gh + b8);
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(gh + b8 + 4);
+      *reinterpret_cast<u32x4_t *>(&sh.hist1[sel_bin(b8)]) = lo;
+      *reinterpret_cast<u32x4_t *>(&sh.hist1[sel_bin(b8) + 4]) = hi;
+      *reinterpret_cast<u32x4_t *>(gh + b8) = u32x4_t{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t *>(gh + b8 + 4) = u32x4_t{0u, 0u, 0u, 0u};
+      if (tid == 0) st[0] = 0u;
+    }
+    const int n = t_last + 1;
+    int32_t *out = tk.indices + row * tk.k;
+    if (n <= tk.k) {
+      for (int i = tid; i < tk.k; i += 256) out[i] = i < n ? i : -1;
+      return;
+    }
+    // every load below max_seq_len <= ld, issued together; candidates past
+    // the row's n are masked inside the selection
+    const int w0 = wv * (kWave * TR);
+    const float *src = scores + row * ld + w0 + lane;
+    const int lim = max_seq_len - w0;
+    float v[TR];
+#pragma unroll
+    for (int u = 0; u < TR; ++u) v[u] = lane < lim - u * kWave ? src[u * kWave] : 0.0f;
+    uint32_t key[TR];
+#pragma unroll
+    for (int u = 0; u < TR; ++u) key[u] = order_key(v[u]);
+    select_run<true>(key, n, tk.k, sh, [&](int u, int slot) { out[slot] = sel_cand<TR>(u); });
   }
 }
 
@@ -811,10 +897,10 @@ hipError_t launch_prefill(const BatchArgs &bt, const void *q_idx, const float *w
   return hipGetLastError();
 }
 
-template <int NMT, int QG, bool FP8, bool PMAX = false>
+template <int NMT, int QG, bool FP8, bool PMAX = false, int TR = 0>
 hipError_t launch_stream(const BatchArgs &bt, const void *q_idx, const float *w,
                          const CacheArgs &keys, float *scores, int64_t ld, hipStream_t stream,
-                         int page_blocks = 1) {
+                         int page_blocks = 1, FusedTopk tk = {}) {
   const int qgroups = (bt.max_q + QG - 1) / QG;
   const int64_t seq_blocks = (bt.max_seq_len + kStreamKeys - 1) / kStreamKeys;
   const int64_t units = (int64_t)qgroups * bt.batch;
@@ -825,15 +911,16 @@ hipError_t launch_stream(const BatchArgs &bt, const void *q_idx, const float *w,
   run = std::min<int64_t>(run, std::max<int64_t>(kStreamBlocks,
                                                  seq_blocks * units / kStreamWorkgroups));
   run = std::min<int64_t>(run, seq_blocks);
+  if (TR > 0 && run > kStreamBlocks) return hipErrorInvalidConfiguration;  // one buffer per run
   const int64_t chunks = (seq_blocks + run - 1) / run;
   if (qgroups > 65535 || bt.batch > 65535 || chunks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)chunks, qgroups, bt.batch);
-  hipLaunchKernelGGL((indexer_stream_kernel<NMT, QG, FP8, PMAX>), grid, dim3(256), 0, stream,
+  hipLaunchKernelGGL((indexer_stream_kernel<NMT, QG, FP8, PMAX, TR>), grid, dim3(256), 0, stream,
                      bt.block_table, bt.seq_lens, bt.cu_q, bt.batch, bt.total_q, bt.max_seq_len,
                      bt.bt_stride, static_cast<const uint16_t *>(q_idx), w,
                      static_cast<const uint8_t *>(keys.data), keys.scale, keys.num_pages,
                      keys.page_size, make_fast_div((uint32_t)keys.page_size), scores, ld, (int)run,
-                     page_blocks);
+                     page_blocks, tk);
   return hipGetLastError();
 }
 
@@ -897,6 +984,21 @@ hipError_t dispatch_page_max(const BatchArgs &bt, const void *q_idx, const float
   }
 }
 
+// Scores plus the fused top-k: one query row per sequence, keys streamed in
+// 64-key blocks; TR candidates per lane of the final selection.
+constexpr int kFusedMaxLen = 256 * 64;  // positions per row (TR = 64)
+
+template <bool FP8, int TR>
+hipError_t dispatch_fused_topk(const BatchArgs &bt, const void *q_idx, const float *w,
+                               int n_heads, const CacheArgs &keys, float *scores, int64_t ld,
+                               FusedTopk tk, hipStream_t stream) {
+  switch (n_heads) {
+    case 16: return launch_stream<1, 1, FP8, false, TR>(bt, q_idx, w, keys, scores, ld, stream, 1, tk);
+    case 32: return launch_stream<2, 1, FP8, false, TR>(bt, q_idx, w, keys, scores, ld, stream, 1, tk);
+    default: return launch_stream<4, 1, FP8, false, TR>(bt, q_idx, w, keys, scores, ld, stream, 1, tk);
+  }
+}
+
 template <typename QT, int KDT>
 hipError_t launch_generic(const BatchArgs &bt, const void *q_idx, const float *w, int H, int D,
                           const CacheArgs &keys, float *scores, int64_t ld, hipStream_t stream) {
@@ -929,6 +1031,34 @@ hipError_t launch_indexer_page_scores(const BatchArgs &bt, const void *q_idx, co
                                    stream);
   return dispatch_page_max<false>(bt, q_idx, w, n_heads, keys, sel_page, page_scores, ld_pages,
                                   stream);
+}
+
+bool indexer_topk_supported(const BatchArgs &bt, int32_t q_dtype, int32_t n_heads,
+                            int32_t head_dim, const CacheArgs &keys) {
+  const bool heads_ok = n_heads == 16 || n_heads == 32 || n_heads == 64;
+  return q_dtype == DSA_BF16 && head_dim == kIdxDim && heads_ok &&
+         (keys.dtype == DSA_BF16 || keys.dtype == DSA_FP8_E4M3) &&
+         keys.page_size % kStreamKeys == 0 && bt.max_q <= 1 && bt.max_seq_len <= kFusedMaxLen;
+}
+
+size_t indexer_topk_state_bytes(int32_t total_q) {
+  return total_q < 1 ? 0 : (size_t)total_q * kFusedRowWords * sizeof(uint32_t);
+}
+
+hipError_t launch_indexer_topk(const BatchArgs &bt, const void *q_idx, const float *w,
+                               int32_t n_heads, const CacheArgs &keys, int32_t k,
+                               int32_t *indices, float *scores, int64_t ld_scores,
+                               uint32_t *state, hipStream_t stream) {
+  if (bt.total_q == 0) return hipSuccess;
+  BatchArgs b = bt;
+  b.max_seq_len = std::max(b.max_seq_len, 1);  // empty rows still get their -1 lists
+  const FusedTopk tk{k, indices, state};
+  const bool fp8 = keys.dtype == DSA_FP8_E4M3;
+  if (b.max_seq_len <= 128 * 64)
+    return fp8 ? dispatch_fused_topk<true, 32>(b, q_idx, w, n_heads, keys, scores, ld_scores, tk, stream)
+               : dispatch_fused_topk<false, 32>(b, q_idx, w, n_heads, keys, scores, ld_scores, tk, stream);
+  return fp8 ? dispatch_fused_topk<true, 64>(b, q_idx, w, n_heads, keys, scores, ld_scores, tk, stream)
+             : dispatch_fused_topk<false, 64>(b, q_idx, w, n_heads, keys, scores, ld_scores, tk, stream);
 }
 
 hipError_t launch_indexer_scores(const BatchArgs &bt, const void *q_idx, int32_t q_dtype,

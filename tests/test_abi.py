@@ -115,6 +115,40 @@ def test_indexer_rejects_bad_arguments(kw, code):
     assert _idx(**kw) == code
 
 
+def _itk(b=None, q=FAKE, qd=L.DSA_BF16, w=FAKE, H=32, D=128, c=None, k=64, s=FAKE, ld=256,
+         idx=FAKE, st=FAKE, stb=1 << 30):
+    b = _batch() if b is None else b
+    c = _cache() if c is None else c
+    return L.lib.dsa_indexer_topk(ctypes.byref(b) if b is not False else None, q, qd, w, H, D,
+                                  ctypes.byref(c) if c is not False else None, k, s, ld, idx,
+                                  st, stb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=False), 1), (dict(q=None), 1), (dict(w=None), 1), (dict(s=None), 1),
+    (dict(idx=None), 1), (dict(c=False), 1),
+    (dict(k=0), 2), (dict(ld=199), 2), (dict(H=0), 2), (dict(D=64), 2), (dict(idx=FAKE + 2), 2),
+    (dict(qd=7), 3), (dict(c=_cache(dtype=9)), 3),
+    # valid, but outside the fused shapes
+    (dict(H=24), 5), (dict(c=_cache(page_size=48), b=_batch(bt_stride=5)), 5),
+    (dict(b=_batch(max_q=2)), 5),
+    (dict(b=_batch(max_seq_len=16385, bt_stride=300), ld=16385), 5),
+    (dict(qd=L.DSA_F32, c=_cache(dtype=L.DSA_F32)), 5),
+    # the per-row state
+    (dict(st=None), 4), (dict(stb=2 * 2112 * 4 - 1), 4), (dict(st=FAKE + 16), 4),
+])
+def test_indexer_topk_rejects_bad_arguments(kw, code):
+    assert _itk(**kw) == code
+
+
+def test_indexer_topk_state_size():
+    assert L.lib.dsa_indexer_topk_state_size(0) == 0
+    assert L.lib.dsa_indexer_topk_state_size(3) == 3 * (64 + 2048) * 4
+    b = L.DsaBatch(block_table=None, seq_lens=None, cu_q=None, batch=0, bt_stride=0, total_q=0,
+                   max_seq_len=0, max_q=0)
+    assert _itk(b=b, q=None, w=None, s=None, idx=None, st=None, stb=0, ld=1) == 0
+
+
 def _topk(b=None, s=FAKE, ld=256, k=64, idx=FAKE, ws=None, wsb=0):
     b = _batch() if b is None else b
     return L.lib.dsa_topk(ctypes.byref(b) if b is not False else None, s, ld, k, idx, ws, wsb, None)

@@ -31,6 +31,12 @@ SMALL_CASES = {
     "bf16_prefill_h64_ragged": small_variant("prefill_q4k_l32k", batch=3, lens=(900, 257, 70),
                                              q_per_seq=(40, 17, 70), idx_heads=64,
                                              page_size=48, topk=128),
+    # prefill kernel, 128-key blocks: 32 heads on pages of 64 (two pages per
+    # block), and 64 heads on pages of 128 (one page per block); ragged tails
+    "bf16_prefill_p64": small_variant("prefill_q4k_l32k", batch=2, lens=(1000, 130),
+                                      q_per_seq=(40, 16), page_size=64, topk=128),
+    "bf16_prefill_h64_p128": small_variant("prefill_q4k_l32k", batch=2, lens=(700, 300),
+                                           q_per_seq=(20, 17), idx_heads=64, topk=128),
     # prefill kernel: 16 heads (32 rows per workgroup), pages of 16
     "bf16_prefill_h16": small_variant("prefill_q4k_l32k", batch=2, lens=(500, 333),
                                       q_per_seq=(33, 20), idx_heads=16, page_size=16, topk=64),
