@@ -152,3 +152,38 @@ def test_several_queries_per_sequence_are_unsupported():
     with pytest.raises(dsa.DSAError) as e:
         dsa.indexer_topk(P.batch_of(inp), inp.q_idx, inp.w, P.keys_of(inp), 256)
     assert e.value.code == 5  # DSA_ERR_UNSUPPORTED
+
+
+def test_graph_replays_match_the_eager_call():
+    """The state clears itself inside the kernel (no memset node), so a captured
+    call replays correctly: three replays with eager calls between them, each
+    equal to the eager result, and the state zero after each."""
+    dsa = _dsa()
+    inp = to_device(make_inputs(small_variant("decode_b32_l8k", batch=4,
+                                              lens=(8192, 3000, 2049, 700), topk=2048)),
+                    torch.device("cuda:0"))
+    k = 2048
+    s_ref, i_ref, _ = _fused(dsa, inp, k)
+    T, ld = inp.total_q, inp.max_seq_len
+    dev = inp.q_idx.device
+    s = torch.zeros((T, ld), dtype=torch.float32, device=dev)
+    i = torch.zeros((T, k), dtype=torch.int32, device=dev)
+    state = torch.zeros(dsa.indexer_topk_state_size(T), dtype=torch.uint8, device=dev)
+    b, keys = P.batch_of(inp), P.keys_of(inp)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):  # warm the call on the capture stream
+        dsa.indexer_topk(b, inp.q_idx, inp.w, keys, k, scores=s, indices=i, state=state)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dsa.indexer_topk(b, inp.q_idx, inp.w, keys, k, scores=s, indices=i, state=state)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        i.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(i, i_ref), "graph replay differs from the eager call"
+        assert int(state.count_nonzero()) == 0, "state not zero-filled after a replay"
+        _fused(dsa, inp, k)  # eager work between replays
