@@ -808,6 +808,10 @@ def main():
                    "parallelism": "single GPU"},
         "achieved_hbm_gbs": ab["total"] / (ms * 1e-3) / 1e9,
         "algorithmic_bytes_per_step": ab["total"],
+        # the fused lower bound: the same step without the token scores' 8 B per
+        # valid (row, position) pair written by the indexer and read by the top-k
+        "algorithmic_bytes_per_step_without_score_round_trip":
+            None if kp else ab["total"] - 8 * ab["valid_pairs"],
         "stage_ms": {n: float(v) for n, v in zip(names, stage_ms)},
         "ms_per_step_stat": "median",
         "ms_per_step_mean": float(np.mean(step_ms)),
