@@ -45,8 +45,10 @@
  *   to [0, num_pages), logical pages past a sequence's length are never read,
  *   rows with zero queries are empty, and indices outside [0, t] are treated
  *   as padding. Malformed metadata thus gives wrong but memory-safe results.
- * - Calls on different streams may run concurrently; the library keeps no
- *   mutable state. A workspace must not be shared by calls that may overlap.
+ * - Calls on different streams may run concurrently; apart from the scratch
+ *   array of dsa_sparse_mla_fwd_noalloc (below), the library keeps no
+ *   mutable state. A workspace, or the state buffer of dsa_indexer_topk,
+ *   must not be shared by calls that may overlap.
  *
  * Row positions. Query rows are flattened over the batch: row r = cu_q[b] + i
  * (0 <= i < q_b = cu_q[b+1] - cu_q[b]) is the token at absolute position
