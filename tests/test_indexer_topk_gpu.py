@@ -34,6 +34,10 @@ CASES = {
                               topk=300),
     # rows past 8K: 64 candidates per lane in the final selection
     "rows_16k": small_variant("decode_b32_l8k", batch=3, lens=(16384, 9000, 8193), topk=2048),
+    # k of one and an odd k, 16 heads on fp8 keys
+    "fp8_h16_k1": small_variant("indexshare_b64", batch=3, lens=(5000, 64, 1), idx_heads=16,
+                                topk=1, n_layers=1),
+    "bf16_k17": small_variant("decode_b32_l8k", batch=3, lens=(3000, 17, 16), topk=17),
     # a sequence without a query row between two with one
     "seq_without_row": small_variant("decode_b32_l8k", batch=3, lens=(700, 300, 65),
                                      q_per_seq=(1, 0, 1), topk=128),
