@@ -85,3 +85,17 @@ def test_mla_rows_and_outputs_are_checked():
     with pytest.raises(ValueError, match="lse must be"):
         dsa.sparse_mla_fwd_layers(_batch(), [q, q], [kv, kv], idx, DL, 0.0625,
                                   lses=[None, torch.zeros((T, 63))])
+
+
+def test_indexer_topk_checks_rows_and_outputs():
+    q = torch.zeros((T, H, D), dtype=torch.bfloat16)
+    w = torch.zeros((T, H))
+    with pytest.raises(ValueError, match="q_idx has 3 rows"):
+        dsa.indexer_topk(_batch(), q[:3], w[:3], _keys(), 64)
+    with pytest.raises(ValueError, match="w must be"):
+        dsa.indexer_topk(_batch(), q, w[:, :16], _keys(), 64)
+    with pytest.raises(ValueError, match="ld >= max_seq_len"):
+        dsa.indexer_topk(_batch(), q, w, _keys(), 64, scores=torch.zeros((T, 200)))
+    with pytest.raises(ValueError, match="indices must be"):
+        dsa.indexer_topk(_batch(), q, w, _keys(), 64, scores=torch.zeros((T, 300)),
+                         indices=torch.zeros((T, 32), dtype=torch.int32))
