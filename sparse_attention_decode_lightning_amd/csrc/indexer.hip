@@ -577,17 +577,21 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
 // alongside the previous block's last), so the barrier between blocks never
 // leaves the matrix core without work.
 //
-// LDS rows are 256 B with their 16-byte chunks XOR-swizzled by the key's low
-// bits, so the 32 keys of one B fragment spread over all bank groups. A lane's
+// Keys reach LDS by direct global-to-LDS copies (two buffers): a block's
+// copies go out at the start of the previous block and are awaited before the
+// barrier that ends it, so no key passes through registers (against staging
+// through registers and LDS stores: 823-837 vs 843-858 us at the 4096-query
+// prefill). LDS rows are 256 B with their 16-byte chunks XOR-swizzled by the
+// key's low bits, applied through the choice of source address, so the 32 keys
+// of one B fragment spread over all bank groups. A lane's
 // head sum covers 16 or 32 of its query's heads; one permlane32 swap adds the
 // other half and leaves lane l with the score of key l of the block, so every
 // query row stores 256 contiguous bytes.
 constexpr int kPfThreads = 512;
 constexpr int kPfWaves = kPfThreads / kWave;
-// Keys per LDS block: 128 for 32 or 64 heads (half the barriers, staging
-// writes and score-store branches per key: 838 vs 865 us at the 4096-query
-// prefill), 64 for 16 heads (whose four query rows per wave leave no
-// registers for a fourth N-tile's staging).
+// Keys per LDS block: 128 for 32 or 64 heads (half the barriers and
+// score-store branches per key: 838 vs 865 us at the 4096-query prefill), 64
+// for 16 heads (a shape no benchmark measures, left at the smaller block).
 template <int H> constexpr int pf_block_keys() { return H == 16 ? 64 : 128; }
 
 
@@ -605,7 +609,6 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
   constexpr int KB = pf_block_keys<H>();                 // keys per LDS block
   constexpr int kNT = KB / 32;                           // 32-key N-tiles per block
   constexpr int kPfChunks = KB * kIdxDim * 2 / 16;       // 16-byte chunks per block
-  constexpr int kPfStage = kPfChunks / kPfThreads;       // staged chunks per thread
   __shared__ u32x4_t kbuf[2][kPfChunks];
 
   const int qblk = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
@@ -653,46 +656,49 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     }
   }
 
-  // Staging: thread tid moves chunk (tid & 15) of keys tid / 16 + 32 * i.
-  const int cw = tid & 15;
-  const int kr0 = tid >> 4;
-  const int lds_chunk = cw ^ (kr0 & 15);
+  // Staging: direct global-to-LDS copies. Copy i of wave wv fills the block's
+  // LDS chunks 64 (8 i + wv) + lane: key 4 (8 i + wv) + lane / 16, slot
+  // lane % 16, which holds the key's global chunk slot ^ (key & 15).
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  constexpr int kCopies = KB / 32;  // per wave per block
   const int64_t bt_row = (int64_t)b * bt_stride;
-  u32x4_t stage[kPfStage];
-  int btv[kPfStage];
-  auto key_pos = [&](int blk, int i) { return min(kbeg + blk * KB + kr0 + 32 * i, t_last); };
+  int btv[kCopies];
+  auto ckey = [&](int i) { return 4 * (8 * i + wv) + (lane >> 4); };
+  auto key_pos = [&](int blk, int i) { return min(kbeg + blk * KB + ckey(i), t_last); };
   auto clamp_page = [&](int64_t page) { return dsa::clamp_page(page, num_pages); };
   auto bt_load = [&](int blk) {
     if constexpr (CONTIG) {
       btv[0] = block_table[bt_row + (int)fast_div((uint32_t)(kbeg + blk * KB), pdiv)];
     } else {
 #pragma unroll
-      for (int i = 0; i < kPfStage; ++i)
+      for (int i = 0; i < kCopies; ++i)
         btv[i] = block_table[bt_row + (int)fast_div((uint32_t)key_pos(blk, i), pdiv)];
     }
   };
-  auto gload = [&](int blk) {
+  auto copy = [&](int blk, int buf) {
+    const lds_u8 *dst0 = (const lds_u8 *)&kbuf[buf][0];
     if constexpr (CONTIG) {
       const int kb0 = kbeg + blk * KB;
       const int pidx = (int)fast_div((uint32_t)kb0, pdiv);
       const int64_t page = clamp_page(btv[0]);
       const uint8_t *base = kdata + (page * page_size + (kb0 - pidx * page_size)) * (2 * kIdxDim);
 #pragma unroll
-      for (int i = 0; i < kPfStage; ++i)
-        stage[i] = ldg16(base + (kr0 + 32 * i) * (2 * kIdxDim) + cw * 16);
+      for (int i = 0; i < kCopies; ++i) {
+        const int key = ckey(i);
+        idx_lds_load16(base + key * (2 * kIdxDim) + 16 * ((lane & 15) ^ (key & 15)),
+                       dst0 + 1024 * (8 * i + wv));
+      }
     } else {
 #pragma unroll
-      for (int i = 0; i < kPfStage; ++i) {
+      for (int i = 0; i < kCopies; ++i) {
+        const int key = ckey(i);
         const int pos = key_pos(blk, i);
         const int in_page = pos - (int)fast_div((uint32_t)pos, pdiv) * page_size;
         const int64_t row = clamp_page(btv[i]) * page_size + in_page;
-        stage[i] = ldg16(kdata + row * (2 * kIdxDim) + cw * 16);
+        idx_lds_load16(kdata + row * (2 * kIdxDim) + 16 * ((lane & 15) ^ (key & 15)),
+                       dst0 + 1024 * (8 * i + wv));
       }
     }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kPfStage; ++i) kbuf[buf][(kr0 + 32 * i) * 16 + lds_chunk] = stage[i];
   };
 
   // B fragment of N-tile n, step s: lane (lh, lc) reads key 32 n + lc, chunk 2 s + lh.
@@ -748,14 +754,11 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
   };
 
   bt_load(0);
-  gload(0);
-  lstore(0);
-  if (nblk > 1) {
-    bt_load(1);
-    gload(1);
-    if (nblk > 2) bt_load(2);
-  }
-  // Every prologue load has landed: the loop then waits only on its own loads.
+  // every compiler-visible load (queries, weights, the first table entry)
+  // lands before the first direct copies, which the compiler does not count
+  __builtin_amdgcn_s_waitcnt(0);
+  copy(0, 0);
+  if (nblk > 1) bt_load(1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -781,6 +784,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
   // block's first half is stored between them)
   for (int blk = 0; blk < nblk; ++blk) {
     const u32x4_t *kb = kbuf[blk & 1];
+    // the other buffer was last read in block blk - 1, before the barrier
+    if (blk + 1 < nblk) copy(blk + 1, (blk & 1) ^ 1);
     mma(kb, 0, acc0);
     epi(acc1, p1);
     phase_order();
@@ -801,13 +806,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
       phase_order();
       pin(p0);
     }
-    if (blk + 1 < nblk) {
-      lstore((blk & 1) ^ 1);
-      if (blk + 2 < nblk) {
-        gload(blk + 2);
-        if (blk + 3 < nblk) bt_load(blk + 3);
-      }
-    }
+    if (blk + 2 < nblk) bt_load(blk + 2);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wave's copies of block blk + 1 landed
     __syncthreads();
   }
   epi(acc1, p1);
