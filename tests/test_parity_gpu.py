@@ -37,6 +37,13 @@ SMALL_CASES = {
                                       q_per_seq=(40, 16), page_size=64, topk=128),
     "bf16_prefill_h64_p128": small_variant("prefill_q4k_l32k", batch=2, lens=(700, 300),
                                            q_per_seq=(20, 17), idx_heads=64, topk=128),
+    # whole key blocks per page on the other block sizes: 16 heads (64-key
+    # blocks) on pages of 64, 32 heads on pages of 256 (two blocks per page)
+    "bf16_prefill_h16_p64": small_variant("prefill_q4k_l32k", batch=2, lens=(700, 200),
+                                          q_per_seq=(40, 16), idx_heads=16, page_size=64,
+                                          topk=64),
+    "bf16_prefill_p256": small_variant("prefill_q4k_l32k", batch=2, lens=(1100, 300),
+                                       q_per_seq=(33, 20), page_size=256, topk=128),
     # prefill kernel: 16 heads (32 rows per workgroup), pages of 16
     "bf16_prefill_h16": small_variant("prefill_q4k_l32k", batch=2, lens=(500, 333),
                                       q_per_seq=(33, 20), idx_heads=16, page_size=16, topk=64),
