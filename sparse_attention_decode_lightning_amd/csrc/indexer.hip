@@ -566,11 +566,11 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
 // [rows x heads, 128] x [128, keys] followed by the per-head ReLU and weighted
 // head sum, and the same keys serve every row of the block. A workgroup of 8
 // waves keeps the query fragments of its rows in registers for its whole key
-// range and streams the keys through LDS in blocks of 128 (64 for 16 heads).
+// range and streams the keys through LDS in blocks of 128.
 //
 // Each wave owns 64 (query, head) rows as two 32-row M-tiles of
 // v_mfma_f32_32x32x16_bf16 (4, 2 or 1 queries for 16, 32 or 64 heads) and a
-// block is four (two) 32-key N-tiles, 8 K-steps each. The 32x32 shape leaves
+// block is four 32-key N-tiles, 8 K-steps each. The 32x32 shape leaves
 // room for about five VALU ops under each 32-cycle MFMA, which the ReLU,
 // weight and head sum (two ops per accumulator element) fit: each N-tile's
 // MFMAs issue alongside the previous N-tile's epilogue (the first one's
@@ -589,10 +589,10 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
 // query row stores 256 contiguous bytes.
 constexpr int kPfThreads = 512;
 constexpr int kPfWaves = kPfThreads / kWave;
-// Keys per LDS block: 128 for 32 or 64 heads (half the barriers and
-// score-store branches per key: 838 vs 865 us at the 4096-query prefill), 64
-// for 16 heads (a shape no benchmark measures, left at the smaller block).
-template <int H> constexpr int pf_block_keys() { return H == 16 ? 64 : 128; }
+// Keys per LDS block (four 32-key N-tiles): against blocks of 64, half the
+// barriers and score-store branches per key (838 vs 865 us at the 4096-query
+// prefill with 32 heads, 476-479 vs 499-514 us with 16).
+constexpr int kPfKeys = 128;
 
 
 // CONTIG: the page size is a multiple of the key block, so each block is
@@ -606,8 +606,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     float *__restrict__ scores, int64_t ld, int keys_per_split, FastDiv pdiv) {
   constexpr int QW = 64 / H;           // query rows per wave
   constexpr int QB = kPfWaves * QW;    // query rows per workgroup
-  constexpr int KB = pf_block_keys<H>();                 // keys per LDS block
+  constexpr int KB = kPfKeys;                            // keys per LDS block
   constexpr int kNT = KB / 32;                           // 32-key N-tiles per block
+  static_assert(kNT == 4, "the block loop below is written for four N-tiles");
   constexpr int kPfChunks = KB * kIdxDim * 2 / 16;       // 16-byte chunks per block
   __shared__ u32x4_t kbuf[2][kPfChunks];
 
@@ -762,9 +763,11 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // Block blk: N-tile 0's MFMAs with the epilogue of block blk - 1's N-tile 1
-  // (zeros before the first block, never stored), then N-tile 1's MFMAs with
-  // N-tile 0's epilogue. The issue pattern interleaves one MFMA with four VALU.
+  // Block blk: N-tile 0's MFMAs with the epilogue of block blk - 1's N-tile 3
+  // (zeros before the first block, never stored), then each N-tile's MFMAs
+  // with the previous N-tile's epilogue; the previous block's second half is
+  // stored after N-tile 0, this block's first half after N-tile 2. The issue
+  // pattern interleaves one MFMA with four VALU.
   f32x16_t acc0[2], acc1[2];
   float p0[QW], p1[QW];
 #pragma unroll
@@ -780,8 +783,6 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
 #pragma unroll
     for (int u = 0; u < QW; ++u) asm volatile("" : "+v"(p[u]));
   };
-  // (with 128-key blocks, N-tiles 2 and 3 repeat the pattern, and the
-  // block's first half is stored between them)
   for (int blk = 0; blk < nblk; ++blk) {
     const u32x4_t *kb = kbuf[blk & 1];
     // the other buffer was last read in block blk - 1, before the barrier
@@ -790,28 +791,26 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     epi(acc1, p1);
     phase_order();
     pin(p1);
-    if (blk > 0) store(blk - 1, kNT / 2 - 1, p0, p1);
+    if (blk > 0) store(blk - 1, 1, p0, p1);
     mma(kb, 1, acc1);
     epi(acc0, p0);
     phase_order();
     pin(p0);
-    if constexpr (kNT == 4) {
-      mma(kb, 2, acc0);
-      epi(acc1, p1);
-      phase_order();
-      pin(p1);
-      store(blk, 0, p0, p1);
-      mma(kb, 3, acc1);
-      epi(acc0, p0);
-      phase_order();
-      pin(p0);
-    }
+    mma(kb, 2, acc0);
+    epi(acc1, p1);
+    phase_order();
+    pin(p1);
+    store(blk, 0, p0, p1);
+    mma(kb, 3, acc1);
+    epi(acc0, p0);
+    phase_order();
+    pin(p0);
     if (blk + 2 < nblk) bt_load(blk + 2);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wave's copies of block blk + 1 landed
     __syncthreads();
   }
   epi(acc1, p1);
-  store(nblk - 1, kNT / 2 - 1, p0, p1);
+  store(nblk - 1, 1, p0, p1);
 }
 
 // Any element types and sizes: one thread per (query row, key position), fp32
@@ -876,7 +875,7 @@ template <int H>
 hipError_t launch_prefill(const BatchArgs &bt, const void *q_idx, const float *w,
                           const CacheArgs &keys, float *scores, int64_t ld, hipStream_t stream) {
   constexpr int QB = kPfWaves * (64 / H);
-  constexpr int KB = pf_block_keys<H>();
+  constexpr int KB = kPfKeys;
   const int qblocks = (bt.max_q + QB - 1) / QB;
   const int kblocks = (bt.max_seq_len + KB - 1) / KB;
   const int64_t units = (int64_t)qblocks * bt.batch;
