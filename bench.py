@@ -154,17 +154,26 @@ def cpu_baseline(inp, budget_s: float, kp: int = 0):
     rng = np.random.default_rng(0)
     order = rng.permutation(inp.total_q)
     done, t0 = 0, time.perf_counter()
+    stage = {"indexer": 0.0, "selection": 0.0, "mla": 0.0}  # seconds per stage, summed
     for r in order:
+        a = time.perf_counter()
         s = O.indexer_scores(host, [int(r)])
+        b = time.perf_counter()
         idx = (O.page_budget_select(s, inp.wl.page_size, kp)[1] if kp
                else O.topk(s, inp.wl.topk))
+        c = time.perf_counter()
         for l in range(inp.wl.n_layers):
             O.sparse_mla(host, l, idx)
+        d = time.perf_counter()
+        stage["indexer"] += b - a
+        stage["selection"] += c - b
+        stage["mla"] += d - c
         done += 1
-        if time.perf_counter() - t0 >= budget_s:
+        if d - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
     return {"value": done / dt, "unit": "query tokens/s", "cores": int(threads), "kind": "oracle",
+            "stage_ms_per_row": {k: 1e3 * v / max(done, 1) for k, v in stage.items()},
             "cores_detail": {"os_cpu_count": os.cpu_count(), "affinity": affinity,
                              "blas_threads": int(threads), "env": env,
                              "note": "the oracle's numpy BLAS threads are the cores it uses"},
